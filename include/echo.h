@@ -1,0 +1,196 @@
+/*
+ * echo.h -- C ABI of libecho: the per-rank compute path of Echo's
+ * error-compensated 4-bit all-reduce on one AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication for
+ * LLM Training and Inference" (arXiv 2610.14277v1).  The all-reduce moves
+ * 4-bit integers and sums in high precision, so every value is quantized at
+ * most twice per call (fugumt page, abstract); a correction built from two
+ * moving averages with different decay rates is added to the input before
+ * each all-reduce, and the averages are refreshed from the output residual
+ * (ai4snews page, "Interpretation").
+ *
+ * One rank's view.  P ranks each hold an n-element bf16 tensor.  Chunk j is
+ * the element range [j*n/P, (j+1)*n/P); rank j owns chunk j.  A call is:
+ *   entry   -- x' = f32(x) - (W_FAST*m_fast + W_SLOW*m_slow); 4-bit group
+ *              quantize x'; chunk j of the message goes to rank j;
+ *   reduce  -- rank p dequantizes the P stage-1 messages of chunk p, sums
+ *              them in binary32 in rank order 0..P-1 and requantizes the sum;
+ *   exit    -- every rank dequantizes the P stage-2 chunks to bf16;
+ *   update  -- r = d1 - x' (+ e2 = f32(y) - S on the own chunk) refreshes
+ *              m_fast <- B_FAST*m_fast + A_FAST*r and
+ *              m_slow <- B_SLOW*m_slow + A_SLOW*r.
+ * There is no transport in this library: the P-1 incoming stage-1 shards and
+ * the P-1 gathered stage-2 chunks are device buffers the caller provides.
+ *
+ * Formats (all device memory, little-endian):
+ *   bf16 tensor   uint16_t[n], bfloat16 bit patterns.
+ *   int4 codes    uint8_t[n/2]; byte k holds element 2k in bits 0..3 and
+ *                 element 2k+1 in bits 4..7, two's complement; the encoder
+ *                 emits codes in [-7, 7] only (a 0x8 field decodes as -8).
+ *   scales        float[n/128]; group g covers elements [128g, 128g+128);
+ *                 element value = code * scale.  Scale 0 means all codes 0.
+ *   averages      float[n] each (m_fast, m_slow), caller-owned.
+ *
+ * Conventions for every call:
+ *   - Returns ECHO_SUCCESS (0) or a negative ECHO_ERR_* code; nothing is
+ *     launched when an argument check fails.  No exception crosses the ABI.
+ *   - Asynchronous: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream).  Calls that touch the same buffers must be ordered by
+ *     the caller (same stream, or events).
+ *   - The library allocates no device memory and keeps no global mutable
+ *     state; every buffer is owned by the caller and must stay valid until
+ *     the enqueued work completes.
+ *   - Alignment: bf16 tensors, codes, averages and e2 arrays must be 16-byte
+ *     aligned; scale arrays 4-byte aligned (ECHO_ERR_ALIGNMENT).
+ *   - Shapes: n > 0, n % (P*128) == 0, n <= ECHO_MAX_ELEMENTS
+ *     (ECHO_ERR_SHAPE); 1 <= P <= ECHO_MAX_RANKS and 0 <= rank < P
+ *     (ECHO_ERR_RANKS).
+ *   - Aliasing: outputs may not overlap each other or any input
+ *     (ECHO_ERR_ALIAS), except that y may equal x exactly (in place) where
+ *     a call takes both; with the phased calls below, run the exit pass
+ *     after the entry pass when y == x.
+ *   - Inputs must be finite; results for inf/NaN inputs, or for sums that
+ *     overflow binary32, are unspecified.
+ *   - Results are deterministic and bit-identical between the fused and the
+ *     unfused sequences.
+ */
+#ifndef ECHO_H
+#define ECHO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- named parameters (readings of what the pages leave open) ------------ */
+#define ECHO_GROUP 128          /* elements per scale */
+#define ECHO_QMAX 7             /* symmetric int4 range [-7, 7] */
+#define ECHO_W_FAST 0.5f        /* correction = W_FAST*m_fast + W_SLOW*m_slow */
+#define ECHO_W_SLOW 0.5f
+#define ECHO_BETA_FAST 0.5f     /* m_fast <- BETA_FAST*m_fast + ALPHA_FAST*r */
+#define ECHO_ALPHA_FAST 0.5f
+#define ECHO_BETA_SLOW 0.875f   /* m_slow <- BETA_SLOW*m_slow + ALPHA_SLOW*r */
+#define ECHO_ALPHA_SLOW 0.125f
+#define ECHO_MAX_RANKS 16
+#define ECHO_MAX_ELEMENTS (INT64_C(1) << 37)
+#define ECHO_ABI_VERSION 1
+
+/* ---- status codes --------------------------------------------------------- */
+#define ECHO_SUCCESS 0
+#define ECHO_ERR_INVALID_ARGUMENT -1 /* a required pointer is NULL */
+#define ECHO_ERR_SHAPE -2            /* n or chunk_n out of range / not a multiple */
+#define ECHO_ERR_ALIGNMENT -3        /* a pointer misses its alignment */
+#define ECHO_ERR_RANKS -4            /* P or rank out of range */
+#define ECHO_ERR_HIP -5              /* the HIP runtime reported an error */
+#define ECHO_ERR_ALIAS -6            /* outputs overlap each other or an input */
+
+typedef void* echo_stream_t; /* a hipStream_t */
+
+/* The compensator of one call sequence (one direction of one model: the
+ * averages are carried from call to call in execution order).  The struct is
+ * plain data owned by the caller; the library reads it and writes only the
+ * two buffers it points to. */
+typedef struct echo_state {
+  float* m_fast; /* device float[n], 16-byte aligned */
+  float* m_slow; /* device float[n], 16-byte aligned */
+  int64_t n;     /* elements of this rank's tensor */
+  int32_t nranks;
+  int32_t rank;
+} echo_state;
+
+typedef struct echo_config {
+  int32_t abi_version, group, qmax, max_ranks;
+  float w_fast, w_slow, beta_fast, alpha_fast, beta_slow, alpha_slow;
+  int64_t max_elements;
+} echo_config;
+
+/* Fill *st and enqueue zero-fills of m_fast and m_slow (the averages start at
+ * zero).  Validates shape, ranks and alignment. */
+int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int32_t nranks,
+                    int32_t rank, echo_stream_t stream);
+
+/* Entry pass over all n elements (ai4snews "Interpretation": the correction
+ * is added to the input before each all-reduce, fused into the entry pass):
+ * x' = f32(x) - (W_FAST*m_fast + W_SLOW*m_slow); per 128-group amax = max|x'|,
+ * s = amax/7 (IEEE division), code = clamp(rint(x'/s), -7, 7); s == 0 gives
+ * codes 0.  Writes codes[n/2] and scales[n/128]; reads the averages, does not
+ * write them. */
+int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* scales,
+                echo_stream_t stream);
+
+/* Reduce stage for one chunk of chunk_n elements (fugumt abstract: 4-bit
+ * transport, high-precision sum, quantized at most twice): shard_codes /
+ * shard_scales are host arrays of nranks device pointers (shard q = rank q's
+ * stage-1 message of this chunk: codes[chunk_n/2], scales[chunk_n/128]).
+ * S = d_0 + d_1 + ... + d_{P-1} in binary32, in that order (d = code*scale);
+ * requantize S like the entry pass -> out_codes[chunk_n/2], out_scales
+ * [chunk_n/128].  Optional outputs (NULL to skip): out_y[chunk_n] =
+ * bf16(code2*s2) rounded to nearest even, out_e2[chunk_n] = f32(y) - S.
+ * chunk_n > 0 and chunk_n % 128 == 0. */
+int echo_reduce_shard(int32_t nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
+                      const float* const* shard_scales, uint8_t* out_codes, float* out_scales,
+                      uint16_t* out_y, float* out_e2, echo_stream_t stream);
+
+/* Exit pass over n elements: y = bf16(code*scale), round to nearest even.
+ * n > 0 and n % 128 == 0. */
+int echo_decode(int64_t n, const uint8_t* codes, const float* scales, uint16_t* y,
+                echo_stream_t stream);
+
+/* Update (ai4snews "Interpretation": the averages are refreshed from the
+ * output residual): with the pre-call averages, recompute x' as the entry
+ * pass does, d1 = code1*scale1, r = d1 - x' plus e2_own[i - rank*n/P] on the
+ * own chunk; then m_fast <- B_FAST*m_fast + A_FAST*r, m_slow <- B_SLOW*m_slow +
+ * A_SLOW*r in place.  codes1/scales1 are this rank's entry-pass output for
+ * all n elements; e2_own is float[n/P]. */
+int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
+                const float* scales1, const float* e2_own, echo_stream_t stream);
+
+/* ---- the fused call, and its three phases --------------------------------- */
+/* The phases split the fused call where a multi-GPU transport would sit:
+ * entry -> (all-to-all of stage-1 chunks) -> reduce -> (all-gather of
+ * stage-2 chunks) -> exit.  echo_call runs all three on one stream and is
+ * bit-identical to echo_encode + echo_reduce_shard + echo_decode +
+ * echo_update. */
+
+/* Entry phase over every chunk except the own one: correction, stage-1
+ * quantization into send_codes[n/2] / send_scales[n/128] (the own chunk's
+ * bytes are left untouched), and the averages' update with r = d1 - x' on
+ * those elements. */
+int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes,
+                    float* send_scales, echo_stream_t stream);
+
+/* Reduce phase over the own chunk: correction and stage-1 quantization of
+ * the own elements (kept in registers, never stored), the rank-order sum with
+ * the P-1 incoming shards recv_codes[q] / recv_scales[q] (host arrays of
+ * nranks device pointers; slot `rank` is ignored and may be NULL; each shard
+ * covers chunk `rank`: codes[n/P/2], scales[n/P/128]), requantization into
+ * own_codes2[n/P/2] / own_scales2[n/P/128], y on the own chunk (y points at
+ * the full n-element output), and the averages' update with r = e1 + e2. */
+int echo_call_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
+                     const float* const* recv_scales, uint8_t* own_codes2, float* own_scales2,
+                     uint16_t* y, echo_stream_t stream);
+
+/* Exit phase over every chunk except the own one: y on chunk j from the
+ * gathered stage-2 chunk gath_codes[j] / gath_scales[j] (host arrays of
+ * nranks device pointers; slot `rank` ignored; each codes[n/P/2],
+ * scales[n/P/128]). */
+int echo_call_exit(const echo_state* st, const uint8_t* const* gath_codes,
+                   const float* const* gath_scales, uint16_t* y, echo_stream_t stream);
+
+/* All three phases, in order, on one stream. */
+int echo_call(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
+              const float* const* recv_scales, const uint8_t* const* gath_codes,
+              const float* const* gath_scales, uint8_t* send_codes, float* send_scales,
+              uint8_t* own_codes2, float* own_scales2, uint16_t* y, echo_stream_t stream);
+
+/* ---- misc ------------------------------------------------------------------ */
+int echo_get_config(echo_config* out);      /* the named parameters above */
+const char* echo_status_string(int status); /* static string, never NULL */
+int echo_version(void);                     /* ECHO_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,353 @@
+"""Pins of the oracle's whole pipeline (CPU only).
+
+What the pages fix and how each is checked:
+  * each value is quantized at most twice per call for any number of GPUs
+    (fugumt abstract; heraldofai "How Echo keeps errors from snowballing"):
+    instrumented counts, and a ring all-reduce that requantizes at every
+    hop as the contrast whose error grows with P;
+  * the sum is formed in high precision and reveals the injected error,
+    which is fed back (ai4snews "Interpretation"; fugumt abstract): the
+    residual identity sum_p r_p = y - sum_p x'_p;
+  * the accumulated error stays bounded independently of depth (fugumt
+    abstract; ai4snews "Perspective"): the deep-chain test, compensated vs
+    uncompensated;
+  * exact-arithmetic re-derivation of a whole call on tiny inputs, and
+    symmetries (power-of-two scaling, negation, P = 1 idempotence).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+
+G = orc.GROUP
+
+
+def bf16_bits(v):
+    t = torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_vals(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def make_ranks(rng, P, n, scale=1.0, state_scale=0.05):
+    xs = [bf16_bits(rng.standard_normal(n) * scale) for _ in range(P)]
+    mf = [(rng.standard_normal(n) * state_scale * scale).astype(np.float32) for _ in range(P)]
+    ms = [(rng.standard_normal(n) * state_scale * scale).astype(np.float32) for _ in range(P)]
+    return xs, mf, ms
+
+
+def copy_states(mf, ms):
+    return [a.copy() for a in mf], [a.copy() for a in ms]
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 16])
+def test_each_value_quantized_exactly_twice(P):
+    rng = np.random.default_rng(P)
+    n = P * G * 2
+    xs, mf, ms = make_ranks(rng, P, n)
+    orc.counters_reset()
+    orc.simulate(xs, mf, ms)
+    # stage 1: each of the P*n input values once; stage 2: each of the n sums once
+    assert orc.counter(1) == P * n
+    assert orc.counter(2) == n
+
+
+def _ring_allreduce(xs_f32):
+    """Contrast: ring reduce-scatter that requantizes the partial sum at every
+    hop, then an all-gather of the quantized total (test-only)."""
+    P = len(xs_f32)
+    n = xs_f32[0].size
+    Cn = n // P
+    out = np.zeros(n, np.float32)
+    for j in range(P):
+        sl = slice(j * Cn, (j + 1) * Cn)
+        acc = None
+        for h in range(P):
+            src = (j + 1 + h) % P
+            part = xs_f32[src][sl] if acc is None else (acc + xs_f32[src][sl]).astype(np.float32)
+            qs = []
+            for g in range(Cn // G):
+                q, s = orc.quantize_group(part[g * G:(g + 1) * G])
+                qs.append(q.astype(np.float32) * np.float32(s))
+            acc = np.concatenate(qs).astype(np.float32)
+        out[sl] = acc
+    return out
+
+
+def test_two_shot_error_flat_in_P_while_ring_grows():
+    rng = np.random.default_rng(7)
+    two_shot, ring = {}, {}
+    for P in (2, 4, 8, 16):
+        n = P * G * 8
+        xs = [bf16_bits(rng.standard_normal(n)) for _ in range(P)]
+        exact = np.sum([bf16_vals(x).astype(np.float64) for x in xs], axis=0)
+        y = bf16_vals(orc.simulate(xs, comp=False)["y"]).astype(np.float64)
+        two_shot[P] = np.sqrt(np.mean((y - exact) ** 2) / np.mean(exact ** 2))
+        yr = _ring_allreduce([bf16_vals(x) for x in xs]).astype(np.float64)
+        ring[P] = np.sqrt(np.mean((yr - exact) ** 2) / np.mean(exact ** 2))
+    assert two_shot[16] < 1.35 * two_shot[2]
+    assert ring[16] > 2.0 * ring[2]
+    assert ring[16] > 2.0 * two_shot[16]
+
+
+def test_single_rank_requantization_is_idempotent():
+    """P = 1: the sum is one dequantized group, so requantizing it returns the
+    same codes."""
+    rng = np.random.default_rng(11)
+    for scale in (1.0, 1e-3, 300.0):
+        x = bf16_bits(rng.standard_normal(G * 16) * scale)
+        codes1, scales1 = orc.encode(x, comp=False)
+        codes2, scales2, _, _ = orc.reduce_chunk([codes1], [scales1], x.size)
+        assert np.array_equal(codes1, codes2)
+        np.testing.assert_allclose(scales2, scales1, rtol=2.0 ** -22)
+
+
+def _simulate_copy(xs, mf, ms, comp=True):
+    mf2, ms2 = copy_states(mf, ms)
+    out = orc.simulate(xs, mf2, ms2, comp=comp)
+    return out, mf2, ms2
+
+
+@pytest.mark.parametrize("k", [3, -5])
+def test_power_of_two_scaling_equivariance(k):
+    rng = np.random.default_rng(20 + k)
+    P, n = 4, 4 * G * 2
+    xs, mf, ms = make_ranks(rng, P, n)
+    out, mf1, ms1 = _simulate_copy(xs, mf, ms)
+    f = np.float32(2.0 ** k)
+    xs_k = [bf16_bits(bf16_vals(x) * f) for x in xs]
+    out_k, mf_k, ms_k = _simulate_copy(xs_k, [a * f for a in mf], [a * f for a in ms])
+    assert np.array_equal(out_k["codes2"], out["codes2"])
+    assert np.array_equal(out_k["scales2"], out["scales2"] * f)
+    assert np.array_equal(bf16_vals(out_k["y"]), bf16_vals(out["y"]) * f)
+    for p in range(P):
+        assert np.array_equal(mf_k[p], mf1[p] * f)
+        assert np.array_equal(ms_k[p], ms1[p] * f)
+
+
+def test_negation_equivariance():
+    rng = np.random.default_rng(30)
+    P, n = 3, 3 * G * 2
+    xs, mf, ms = make_ranks(rng, P, n)
+    out, mf1, ms1 = _simulate_copy(xs, mf, ms)
+    xs_n = [x ^ np.uint16(0x8000) for x in xs]
+    out_n, mf_n, ms_n = _simulate_copy(xs_n, [-a for a in mf], [-a for a in ms])
+    q = orc.unpack(out["codes2"], n)
+    q_n = orc.unpack(out_n["codes2"], n)
+    assert np.array_equal(q_n, -q)
+    assert np.array_equal(out_n["scales2"], out["scales2"])
+    assert np.array_equal(bf16_vals(out_n["y"]), -bf16_vals(out["y"]))
+    for p in range(P):
+        assert np.array_equal(mf_n[p], -mf1[p]) and np.array_equal(ms_n[p], -ms1[p])
+
+
+@pytest.mark.parametrize("P", [2, 3, 8])
+def test_residual_identity(P):
+    """The residuals the ranks fold into their averages add up to the error
+    the call injected: sum_p r_p = f32(y) - sum_p x'_p, up to the binary32
+    rounding of the rank-order sum and of each residual."""
+    rng = np.random.default_rng(40 + P)
+    n = P * G * 4
+    xs, mf, ms = make_ranks(rng, P, n, state_scale=0.1)
+    out = orc.simulate(xs, mf, ms, want_detail=True)
+    y = bf16_vals(out["y"]).astype(np.float64)
+    xp = np.array(out["xp"], dtype=np.float64)
+    r = np.array(out["r"], dtype=np.float64)
+    lhs = r.sum(axis=0)
+    rhs = y - xp.sum(axis=0)
+    d1 = []
+    for p in range(P):
+        q = orc.unpack(out["codes1"][p], n).astype(np.float64)
+        d1.append(q * np.repeat(out["scales1"][p].astype(np.float64), G))
+    d1 = np.abs(np.array(d1)).sum(axis=0)
+    u = 2.0 ** -24
+    bound = 4 * P * u * (np.abs(xp).sum(axis=0) + d1 + np.abs(y) + np.abs(r).sum(axis=0))
+    assert np.all(np.abs(lhs - rhs) <= bound)
+    # and the injected error is not trivially zero
+    assert np.sqrt(np.mean(rhs ** 2)) > 1e-3
+
+
+def test_compensation_off_matches_first_call_from_zero_state():
+    rng = np.random.default_rng(50)
+    P, n = 4, 4 * G * 2
+    xs = [bf16_bits(rng.standard_normal(n)) for _ in range(P)]
+    zeros = [np.zeros(n, np.float32) for _ in range(P)]
+    on = orc.simulate(xs, [z.copy() for z in zeros], [z.copy() for z in zeros])
+    off = orc.simulate(xs, comp=False)
+    for key in ("codes2", "scales2", "y"):
+        assert np.array_equal(on[key], off[key])
+
+
+@pytest.mark.parametrize("P,chunks", [(2, 1), (4, 3), (8, 2)])
+def test_rank_mode_reproduces_simulation(P, chunks):
+    """Rank p fed the other ranks' stage-1 chunks and the gathered stage-2
+    chunks reproduces the simulated call: send message, own stage-2 chunk,
+    output and updated state."""
+    rng = np.random.default_rng(60 + P)
+    n = P * G * chunks
+    Cn = n // P
+    xs, mf, ms = make_ranks(rng, P, n, state_scale=0.1)
+    mf0, ms0 = copy_states(mf, ms)
+    sim = orc.simulate(xs, mf, ms, want_detail=True)
+    for p in range(P):
+        cs = slice(p * Cn // 2, (p + 1) * Cn // 2)
+        ss = slice(p * Cn // G, (p + 1) * Cn // G)
+        recv_c = [None if q == p else sim["codes1"][q][cs].copy() for q in range(P)]
+        recv_s = [None if q == p else sim["scales1"][q][ss].copy() for q in range(P)]
+        gath_c = [None if j == p else sim["codes2"][j * Cn // 2:(j + 1) * Cn // 2].copy()
+                  for j in range(P)]
+        gath_s = [None if j == p else sim["scales2"][j * Cn // G:(j + 1) * Cn // G].copy()
+                  for j in range(P)]
+        mfp, msp = mf0[p].copy(), ms0[p].copy()
+        out = orc.call(P, p, xs[p], mfp, msp, recv_c, recv_s, gath_c, gath_s)
+        assert np.array_equal(out["y"], sim["y"])
+        assert np.array_equal(out["own_codes2"], sim["codes2"][cs])
+        assert np.array_equal(out["own_scales2"], sim["scales2"][ss])
+        for j in range(P):
+            if j != p:
+                jc = slice(j * Cn // 2, (j + 1) * Cn // 2)
+                assert np.array_equal(out["send_codes"][jc], sim["codes1"][p][jc])
+        assert np.array_equal(mfp, mf[p]) and np.array_equal(msp, ms[p])
+
+
+# ---- exact re-derivation on tiny inputs ---------------------------------------------
+
+def _exact_quant(vals):
+    """Real-number group quantizer: s = amax/7 exactly, nearest code (ties even).
+    Returns (codes, s, margin) where margin is the distance of v/s to the
+    nearest half-integer (small margins can flip under binary32 rounding)."""
+    amax = max(abs(v) for v in vals)
+    if amax == 0:
+        return [0] * len(vals), Fraction(0), [Fraction(1)] * len(vals)
+    s = amax / 7
+    codes, margins = [], []
+    for v in vals:
+        t = v / s
+        c = min(range(-7, 8), key=lambda c: (abs(t - c), c % 2))
+        fl = t - (t.numerator // t.denominator)
+        codes.append(c)
+        margins.append(abs(fl - Fraction(1, 2)))
+    return codes, s, margins
+
+
+@pytest.mark.parametrize("P,k", [(1, 1), (2, 1), (2, 2), (3, 1), (3, 2), (4, 2)])
+def test_bruteforce_against_exact_arithmetic(P, k):
+    """A whole compensated call re-derived with rational arithmetic (no
+    binary32 rounding anywhere) agrees with the oracle: codes exactly wherever
+    no quotient sits within 2^-14 of a rounding boundary, scales to 2^-20
+    relative, outputs to one bf16 step and averages to binary32 rounding."""
+    rng = np.random.default_rng(100 * P + k)
+    n = P * G * k
+    Cn = n // P
+    xs, mf, ms = make_ranks(rng, P, n, state_scale=0.2)
+    mf0, ms0 = copy_states(mf, ms)
+    sim = orc.simulate(xs, mf, ms, want_detail=True)
+    F = Fraction
+    half = F(1, 2)
+    eps = F(1, 1 << 14)
+    # stage 1, real numbers
+    xp = [[F(float(a)) - (half * F(float(b)) + half * F(float(c)))
+           for a, b, c in zip(bf16_vals(xs[p]).tolist(), mf0[p].tolist(), ms0[p].tolist())]
+          for p in range(P)]
+    d1, q1, s1, ok1 = [], [], [], []
+    for p in range(P):
+        qp, dp, sp, okp = [], [], [], []
+        for g in range(n // G):
+            c, s, m = _exact_quant(xp[p][g * G:(g + 1) * G])
+            qp += c
+            sp.append(s)
+            dp += [ci * s for ci in c]
+            okp += [mi > eps for mi in m]
+        d1.append(dp), q1.append(qp), s1.append(sp), ok1.append(okp)
+    safe_groups = set()
+    for p in range(P):
+        oq = orc.unpack(sim["codes1"][p], n)
+        for g in range(n // G):
+            sl = range(g * G, (g + 1) * G)
+            good = all(ok1[p][i] for i in sl)
+            if good:
+                assert [int(oq[i]) for i in sl] == q1[p][g * G:(g + 1) * G]
+                assert abs(F(float(sim["scales1"][p][g])) - s1[p][g]) <= s1[p][g] * F(1, 1 << 20)
+            else:
+                safe_groups.add(g)  # mark as unsafe for stage 2
+    unsafe = safe_groups
+    # stage 2 and the residual, real numbers
+    S = [sum(d1[p][i] for p in range(P)) for i in range(n)]
+    oq2 = orc.unpack(sim["codes2"], n)
+    oy = bf16_vals(sim["y"]).astype(np.float64)
+    n_checked = 0
+    for g in range(n // G):
+        if g in unsafe:
+            continue
+        c2, s2, m2 = _exact_quant(S[g * G:(g + 1) * G])
+        if not all(mi > eps for mi in m2):
+            continue
+        assert [int(oq2[i]) for i in range(g * G, (g + 1) * G)] == c2
+        assert abs(F(float(sim["scales2"][g])) - s2) <= s2 * F(1, 1 << 20)
+        for i in range(g * G, (g + 1) * G):
+            yv = float(c2[i - g * G] * s2)
+            assert abs(oy[i] - yv) <= abs(yv) * 2.0 ** -8 + 1e-30
+            # residual and averages on this element, every rank
+            e2 = F(float(oy[i])) - S[i]
+            for p in range(P):
+                r = d1[p][i] - xp[p][i] + (e2 if i // Cn == p else 0)
+                want_f = half * F(float(mf0[p][i])) + half * r
+                want_s = F(7, 8) * F(float(ms0[p][i])) + F(1, 8) * r
+                tol = F(1, 1 << 20) * (abs(xp[p][i]) + abs(S[i]) + abs(F(float(mf0[p][i])))
+                                        + abs(F(float(ms0[p][i]))) + abs(d1[p][i]) + 1e-30)
+                assert abs(F(float(mf[p][i])) - want_f) <= tol
+                assert abs(F(float(ms[p][i])) - want_s) <= tol
+            n_checked += 1
+    assert n_checked >= n // 2
+
+
+# ---- deep chain -----------------------------------------------------------------------
+
+def _chain(comp, L, P=8, n=8 * G * 2, seed=0):
+    rng = np.random.default_rng(seed)
+    mf = [np.zeros(n, np.float32) for _ in range(P)]
+    ms = [np.zeros(n, np.float32) for _ in range(P)]
+    h = np.zeros(n)
+    H = np.zeros(n)
+    errs, inj = {}, []
+    for l in range(1, L + 1):
+        xs = [bf16_bits(rng.standard_normal(n)) for _ in range(P)]
+        out = orc.simulate(xs, mf, ms, comp=comp, want_detail=comp)
+        y = bf16_vals(out["y"]).astype(np.float64)
+        xsum = np.sum([bf16_vals(x).astype(np.float64) for x in xs], axis=0)
+        xpsum = np.sum(out["xp"], axis=0, dtype=np.float64) if comp else xsum
+        inj.append(np.sqrt(np.mean((y - xpsum) ** 2)))
+        h += y
+        H += xsum
+        if l & (l - 1) == 0:
+            errs[l] = np.sqrt(np.mean((h - H) ** 2))
+    return errs, float(np.mean(inj))
+
+
+def _slope(errs, lo=16):
+    Ls = np.array([L for L in errs if L >= lo], dtype=np.float64)
+    e = np.array([errs[int(L)] for L in Ls])
+    return np.polyfit(np.log(Ls), np.log(e), 1)[0]
+
+
+def test_deep_chain_compensated_bounded_uncompensated_grows():
+    """Accumulated deviation of a residual stream fed by L calls: bounded
+    independently of depth with the compensator, growing like sqrt(L)
+    without it.  With the chosen averages the bounded level is
+    sqrt(sum_n K(n)^2) = sqrt(2.289) ~ 1.5 times one call's injected error,
+    where K(n) = W_F B_F^n + W_S B_S^n."""
+    L = 256
+    on, inj_on = _chain(True, L)
+    off, inj_off = _chain(False, L)
+    ratio_on = {k: v / inj_on for k, v in on.items()}
+    ratio_off = {k: v / inj_off for k, v in off.items()}
+    assert max(ratio_on.values()) <= 3.0
+    assert 0.8 <= ratio_on[L] <= 2.5
+    assert _slope(on) < 0.1
+    assert _slope(off) > 0.4
+    assert ratio_off[L] > 8.0  # ~ sqrt(256) = 16 for independent errors
