@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused Echo rank pipeline on one MI355X.
+
+Workload (default): a 1 GB message -- one rank's bf16 vector of 2^29
+elements, N(0,1) with 0.1% of elements x20, P = 8 logical ranks, this rank 0,
+group 128; the 7 incoming stage-1 shards of this rank's 2^26-element chunk
+and the 7 gathered stage-2 chunks are seeded int4 messages resident in HBM.
+The averages are carried across calls.  A step is one call: the entry phase
+(K_entry), the own-chunk reduce phase (K_reduce) and the exit phase
+(K_exit) -- exactly the launches echo_call makes -- on one stream.
+
+Prints one JSON line: payload GB/s (2 bytes per element per call), the
+roofline of the dominant kernel (K_entry) from HIP events recorded on the
+launch stream inside the timed region, and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GB/s of bf16 payload through fused Echo rank pipeline @1GB msg; % HBM peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
+
+
+def bytes_per_element(P: int) -> dict:
+    """Algorithmic HBM bytes per element of each kernel's range."""
+    code = 0.5 + 4.0 / 128.0  # packed nibble + share of the fp32 group scale
+    return {
+        "entry": 2 + 8 + 8 + code,             # x, 2 averages in, 2 out, send message
+        "reduce": 2 + 8 + 8 + 2 + code * P,    # x, averages in/out, y, P-1 shards in + codes2 out
+        "exit": code + 2,                      # gathered message in, y out
+    }
+
+
+def step_bytes(N: int, P: int) -> float:
+    b = bytes_per_element(P)
+    C = N // P
+    return (N - C) * b["entry"] + C * b["reduce"] + (N - C) * b["exit"]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("error_compensated_bit_echo_amd/csrc/echo_device.h",
+                "error_compensated_bit_echo_amd/csrc/echo_api.hip",
+                "error_compensated_bit_echo_amd/build.py"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def make_workload(N: int, P: int, rank: int, seed: int = 0):
+    import numpy as np
+
+    from error_compensated_bit_echo_amd import inputs as I
+
+    C = N // P
+    x = I.vector_with_outliers(N, I.stream_key("echo-1gb", seed, "x"), outlier_mult=20.0)
+    recv = [None if q == rank else I.int4_message(C, I.stream_key("echo-1gb", seed, "recv", q))
+            for q in range(P)]
+    # gathered stage-2 chunks carry sums of P contributions: larger scales
+    gath = [None if j == rank else
+            I.int4_message(C, I.stream_key("echo-1gb", seed, "gath", j),
+                           scale_lo=0.05 * np.sqrt(P), scale_hi=0.55 * np.sqrt(P))
+            for j in range(P)]
+    return x, recv, gath
+
+
+def cpu_baseline(x, recv, gath, P: int, rank: int, n_sample: int, calls: int):
+    """The CPU oracle as it stands (one thread), rank-mode calls on the first
+    n_sample elements of the same workload (the sample's chunks are prefixes
+    of the workload's shards), the averages carried; payload GB/s."""
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    Cs = n_sample // P
+    xs = np.ascontiguousarray(x[:n_sample])
+    rc = [None if m is None else np.ascontiguousarray(m[0][:Cs // 2]) for m in recv]
+    rs = [None if m is None else np.ascontiguousarray(m[1][:Cs // 128]) for m in recv]
+    gc = [None if m is None else np.ascontiguousarray(m[0][:Cs // 2]) for m in gath]
+    gs = [None if m is None else np.ascontiguousarray(m[1][:Cs // 128]) for m in gath]
+    mf = np.zeros(n_sample, np.float32)
+    ms = np.zeros(n_sample, np.float32)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        orc.call(P, rank, xs, mf, ms, rc, rs, gc, gs)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(2.0 * n_sample * calls / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{calls} rank-mode calls (P={P}, rank {rank}) on the first {n_sample} "
+                   f"elements of the workload, averages carried; {dt:.1f} s on 1 thread"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--log2n", type=int, default=29, help="elements per rank = 2^log2n")
+    ap.add_argument("--nranks", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-log2n", type=int, default=26)
+    ap.add_argument("--cpu-calls", type=int, default=24)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures the per-rank pipeline on one GPU; this build has no "
+              "multi-GPU transport, so --gpus must be 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from error_compensated_bit_echo_amd import binding as B
+
+    N, P, rank = 1 << args.log2n, args.nranks, 0
+    C = N // P
+    dev = torch.device("cuda:0")
+    print(f"bench: generating workload N={N} P={P}", file=sys.stderr, flush=True)
+    x, recv, gath = make_workload(N, P, rank)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    xd = d(x)
+    rd = [None if m is None else (d(m[0]), d(m[1])) for m in recv]
+    gd = [None if m is None else (d(m[0]), d(m[1])) for m in gath]
+    mf = torch.empty(N, dtype=torch.float32, device=dev)
+    ms = torch.empty(N, dtype=torch.float32, device=dev)
+    send_c = torch.empty(N // 2, dtype=torch.uint8, device=dev)
+    send_s = torch.empty(N // 128, dtype=torch.float32, device=dev)
+    own_c = torch.empty(C // 2, dtype=torch.uint8, device=dev)
+    own_s = torch.empty(C // 128, dtype=torch.float32, device=dev)
+    y = torch.empty(N, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    st = B.echo_state_init(mf, ms, N, P, rank, stream)
+    rc_ = [None if m is None else m[0] for m in rd]
+    rs_ = [None if m is None else m[1] for m in rd]
+    gc_ = [None if m is None else m[0] for m in gd]
+    gs_ = [None if m is None else m[1] for m in gd]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.echo_call_entry(st, xd, send_c, send_s, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.echo_call_reduce(st, xd, rc_, rs_, own_c, own_s, y, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        B.echo_call_exit(st, gc_, gs_, y, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print(f"bench: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = {
+        "entry": float(np.mean([e[0].elapsed_time(e[1]) for e in events])),
+        "reduce": float(np.mean([e[1].elapsed_time(e[2]) for e in events])),
+        "exit": float(np.mean([e[2].elapsed_time(e[3]) for e in events])),
+    }
+
+    # the fused entry point itself, same stream, for reference
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        B.echo_call(st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, y, stream)
+    torch.cuda.synchronize()
+    call_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+
+    bpe = bytes_per_element(P)
+    entry_bytes = (N - C) * bpe["entry"]
+    achieved = entry_bytes / (k_ms["entry"] * 1e-3) / 1e9
+    total_bytes = step_bytes(N, P)
+    workload = f"1GB message: bf16[2^{args.log2n}] per rank, P={P}, rank {rank}, group 128"
+    out = {
+        "metric": METRIC,
+        "value": round(2.0 * N / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "elements": N, "nranks": P, "rank": rank, "group": 128,
+                   "input": "N(0,1), 0.1% of elements x20; seeded int4 shards in HBM"},
+        "pct_hbm_peak": round(100.0 * total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "algorithmic_bytes_per_step": int(total_bytes),
+        "kernel_ms": {k: round(v, 4) for k, v in k_ms.items()},
+        "echo_call_ms": round(call_ms, 4),
+        "roofline": {
+            "kernel": "K_entry (k_stage1<entry>)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile("entry", "1gb") if args.log2n == 29 and P == 8 else None,
+            "bytes_per_launch": int(entry_bytes),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        n_s = min(N, 1 << args.cpu_log2n)
+        out["cpu_baseline"] = cpu_baseline(x, recv, gath, P, rank, n_s, args.cpu_calls)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,196 @@
+"""Thin Python binding of libecho (include/echo.h).
+
+Argument marshalling only: every step of the pipeline runs in the HIP
+kernels of libecho.so.  PyTorch provides device memory and streams: tensors
+are passed by address, the stream defaults to torch's current stream.
+
+Functions keep the C names (echo_state_init, echo_encode, ...) and raise
+EchoError on a non-zero status.  There is no fallback: if libecho.so is
+missing the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch  # load torch's HIP runtime first: libecho binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libecho.so")
+
+GROUP = 128
+MAX_RANKS = 16
+
+
+class EchoError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class EchoStateC(C.Structure):
+    _fields_ = [("m_fast", C.c_void_p), ("m_slow", C.c_void_p), ("n", C.c_int64),
+                ("nranks", C.c_int32), ("rank", C.c_int32)]
+
+
+class EchoConfigC(C.Structure):
+    _fields_ = [("abi_version", C.c_int32), ("group", C.c_int32), ("qmax", C.c_int32),
+                ("max_ranks", C.c_int32), ("w_fast", C.c_float), ("w_slow", C.c_float),
+                ("beta_fast", C.c_float), ("alpha_fast", C.c_float), ("beta_slow", C.c_float),
+                ("alpha_slow", C.c_float), ("max_elements", C.c_int64)]
+
+
+_vp = C.c_void_p
+_pp = C.POINTER(C.c_void_p)
+_SIGNATURES = {
+    "echo_state_init": [C.POINTER(EchoStateC), _vp, _vp, C.c_int64, C.c_int32, C.c_int32, _vp],
+    "echo_encode": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp],
+    "echo_reduce_shard": [C.c_int32, C.c_int64, _pp, _pp, _vp, _vp, _vp, _vp, _vp],
+    "echo_decode": [C.c_int64, _vp, _vp, _vp, _vp],
+    "echo_update": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp, _vp],
+    "echo_call_entry": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp],
+    "echo_call_reduce": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp, _vp, _vp],
+    "echo_call_exit": [C.POINTER(EchoStateC), _pp, _pp, _vp, _vp],
+    "echo_call": [C.POINTER(EchoStateC), _vp, _pp, _pp, _pp, _pp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "echo_get_config": [C.POINTER(EchoConfigC)],
+    "echo_status_string": [C.c_int],
+    "echo_version": [],
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libecho.so not built at {LIB_PATH}; run __graft_entry__.build()")
+    lib = C.CDLL(LIB_PATH)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = C.c_char_p if name == "echo_status_string" else C.c_int
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.echo_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise EchoError(status, where)
+
+
+def _ptr(t):
+    """Device address of a tensor (None -> NULL); plain ints pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ptrs(ts):
+    # at least MAX_RANKS slots: entries past the list are NULL, which the
+    # library rejects instead of reading past the array
+    arr = (C.c_void_p * max(MAX_RANKS, len(ts)))()
+    for i, t in enumerate(ts):
+        arr[i] = _ptr(t)
+    return C.cast(arr, _pp)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class EchoState:
+    """Compensator state of one call sequence: two float32 averages of n
+    elements (caller-owned tensors), P ranks, this rank."""
+
+    def __init__(self, m_fast: torch.Tensor, m_slow: torch.Tensor, n: int, nranks: int, rank: int):
+        self.m_fast, self.m_slow = m_fast, m_slow  # keep the buffers alive
+        self.c = EchoStateC(_ptr(m_fast), _ptr(m_slow), int(n), int(nranks), int(rank))
+
+    @property
+    def n(self) -> int:
+        return self.c.n
+
+    @property
+    def nranks(self) -> int:
+        return self.c.nranks
+
+    @property
+    def rank(self) -> int:
+        return self.c.rank
+
+
+def echo_state_init(m_fast, m_slow, n, nranks, rank, stream=None) -> EchoState:
+    st = EchoState(m_fast, m_slow, n, nranks, rank)
+    _check(lib.echo_state_init(C.byref(st.c), _ptr(m_fast), _ptr(m_slow), int(n), int(nranks),
+                               int(rank), _stream(stream)), "echo_state_init")
+    return st
+
+
+def echo_encode(st: EchoState, x, codes, scales, stream=None) -> None:
+    _check(lib.echo_encode(C.byref(st.c), _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)),
+           "echo_encode")
+
+
+def echo_reduce_shard(shard_codes, shard_scales, out_codes, out_scales, out_y=None, out_e2=None,
+                      chunk_n=None, stream=None) -> None:
+    P = len(shard_codes)
+    if chunk_n is None:
+        chunk_n = out_codes.numel() * 2
+    _check(lib.echo_reduce_shard(P, int(chunk_n), _ptrs(shard_codes), _ptrs(shard_scales),
+                                 _ptr(out_codes), _ptr(out_scales), _ptr(out_y), _ptr(out_e2),
+                                 _stream(stream)), "echo_reduce_shard")
+
+
+def echo_decode(codes, scales, y, n=None, stream=None) -> None:
+    if n is None:
+        n = y.numel()
+    _check(lib.echo_decode(int(n), _ptr(codes), _ptr(scales), _ptr(y), _stream(stream)),
+           "echo_decode")
+
+
+def echo_update(st: EchoState, x, codes1, scales1, e2_own, stream=None) -> None:
+    _check(lib.echo_update(C.byref(st.c), _ptr(x), _ptr(codes1), _ptr(scales1), _ptr(e2_own),
+                           _stream(stream)), "echo_update")
+
+
+def echo_call_entry(st: EchoState, x, send_codes, send_scales, stream=None) -> None:
+    _check(lib.echo_call_entry(C.byref(st.c), _ptr(x), _ptr(send_codes), _ptr(send_scales),
+                               _stream(stream)), "echo_call_entry")
+
+
+def echo_call_reduce(st: EchoState, x, recv_codes, recv_scales, own_codes2, own_scales2, y,
+                     stream=None) -> None:
+    _check(lib.echo_call_reduce(C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
+                                _ptr(own_codes2), _ptr(own_scales2), _ptr(y), _stream(stream)),
+           "echo_call_reduce")
+
+
+def echo_call_exit(st: EchoState, gath_codes, gath_scales, y, stream=None) -> None:
+    _check(lib.echo_call_exit(C.byref(st.c), _ptrs(gath_codes), _ptrs(gath_scales), _ptr(y),
+                              _stream(stream)), "echo_call_exit")
+
+
+def echo_call(st: EchoState, x, recv_codes, recv_scales, gath_codes, gath_scales, send_codes,
+              send_scales, own_codes2, own_scales2, y, stream=None) -> None:
+    _check(lib.echo_call(C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
+                         _ptrs(gath_codes), _ptrs(gath_scales), _ptr(send_codes),
+                         _ptr(send_scales), _ptr(own_codes2), _ptr(own_scales2), _ptr(y),
+                         _stream(stream)), "echo_call")
+
+
+def echo_get_config() -> dict:
+    cfg = EchoConfigC()
+    _check(lib.echo_get_config(C.byref(cfg)), "echo_get_config")
+    return {name: getattr(cfg, name) for name, _ in EchoConfigC._fields_}
+
+
+def echo_version() -> int:
+    return int(lib.echo_version())

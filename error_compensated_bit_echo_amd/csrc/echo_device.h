@@ -1,0 +1,430 @@
+// echo_device.h -- gfx950 device code of libecho: the Echo rank pipeline
+// (arXiv 2610.14277v1; ai4snews page "Interpretation" for the compensator,
+// fugumt abstract for the 4-bit transport with a high-precision sum).
+//
+// Work layout.  Every kernel walks 128-element quantization groups.  The
+// stage-1 / reduce kernels give each 64-lane wavefront a "slice" of two
+// consecutive groups per step: lane l holds 4 consecutive elements, lanes
+// 0-31 form the first group and lanes 32-63 the second, so every global
+// access of a wave is one contiguous run (x: 512 B, each average: 1 KiB,
+// codes: 128 B) and a group's absmax is a 32-lane reduction done with DPP
+// row operations plus one ds_swizzle (no LDS traffic, no barrier).  The exit
+// kernel gives each lane 8 elements (a group is one 16-lane DPP row).
+//
+// Arithmetic.  Built with -ffp-contract=off: each float operation below is
+// one IEEE binary32 operation rounded to nearest even, denormals kept;
+// x'/s is the correctly rounded division; rint is v_rndne_f32; the bf16
+// narrowing is the hardware round-to-nearest-even convert.  The operation
+// order is the method's: corr = (W_F*m_f) + (W_S*m_s); x' = f32(x) - corr;
+// S = d_0 + d_1 + ... in rank order; m <- (B*m) + (A*r).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "echo.h"
+
+namespace echo {
+
+constexpr int kGroup = ECHO_GROUP;
+constexpr float kQmax = (float)ECHO_QMAX;
+constexpr int kMaxRanks = ECHO_MAX_RANKS;
+constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
+
+// ---------------------------------------------------------------------------
+// lane-level helpers
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// max over the 32 lanes of each half-wave (all 64 lanes must be active).
+// Bit patterns of non-negative floats order like the floats themselves.
+__device__ __forceinline__ uint32_t halfwave_max(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = max(v, dpp_u32<0x141>(v));  // row_half_mirror: quad 0 <-> quad 1
+  v = max(v, dpp_u32<0x140>(v));  // row_mirror: half-row 0 <-> half-row 1
+  // bitmask swizzle (and 0x1F, or 0, xor 0x10): row 0 <-> row 1 in each 32
+  v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
+  return v;
+}
+
+// max over each 16-lane row (all 64 lanes must be active).
+__device__ __forceinline__ uint32_t row_max(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// bf16 bits -> binary32 (exact)
+__device__ __forceinline__ void unpack_bf16x4(uint2 w, float (&f)[4]) {
+  f[0] = __uint_as_float(w.x << 16);
+  f[1] = __uint_as_float(w.x & 0xFFFF0000u);
+  f[2] = __uint_as_float(w.y << 16);
+  f[3] = __uint_as_float(w.y & 0xFFFF0000u);
+}
+
+// two binary32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  f2 v = {a, b};
+  h2 h = __builtin_convertvector(v, h2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// x' = f32(x) - ((W_F*m_f) + (W_S*m_s))
+__device__ __forceinline__ float corrected(float xf, float mf, float ms) {
+  float corr = (ECHO_W_FAST * mf) + (ECHO_W_SLOW * ms);
+  return xf - corr;
+}
+
+// The group scale from the group's absmax: s = amax / 7 (IEEE division).
+__device__ __forceinline__ float scale_of(uint32_t amax_bits) {
+  return __uint_as_float(amax_bits) / kQmax;
+}
+
+// Divisor used for the codes: s itself, or 1 when s == 0.  s == 0 means
+// amax <= 3 * 2^-149 (all-zero group, or amax/7 underflowing), where every
+// |v| / 1 < 0.5 rounds to code 0 -- the same codes as the zero-group rule.
+__device__ __forceinline__ float code_divisor(float s) { return s == 0.0f ? 1.0f : s; }
+
+// code = clamp(rint(v / s), -7, 7)
+__device__ __forceinline__ int quant_code(float v, float sdiv) {
+  float t = __builtin_rintf(v / sdiv);
+  t = fminf(fmaxf(t, -kQmax), kQmax);
+  return (int)t;
+}
+
+// 4 codes -> 16 bits, element k in bits 4k..4k+3 (two's complement nibbles)
+__device__ __forceinline__ uint32_t pack_nib4(const int (&q)[4]) {
+  return ((uint32_t)q[0] & 0xFu) | (((uint32_t)q[1] & 0xFu) << 4) |
+         (((uint32_t)q[2] & 0xFu) << 8) | (((uint32_t)q[3] & 0xFu) << 12);
+}
+
+// nibble k of a packed word -> signed code (sign-extend the 4-bit field)
+__device__ __forceinline__ int nib(uint32_t w, int k) {
+  return (int)(w << (28 - 4 * k)) >> 28;
+}
+
+// m <- (B*m) + (A*r) for both averages
+__device__ __forceinline__ void refresh(float& mf, float& ms, float r) {
+  mf = (ECHO_BETA_FAST * mf) + (ECHO_ALPHA_FAST * r);
+  ms = (ECHO_BETA_SLOW * ms) + (ECHO_ALPHA_SLOW * r);
+}
+
+// ---------------------------------------------------------------------------
+// stage-1 kernel: entry pass / plain encode / plain update
+
+enum Stage1Mode { kEncode = 0, kEntryFused = 1, kUpdate = 2 };
+
+struct Stage1Args {
+  const uint16_t* x;      // [n]
+  float* mf;              // [n]
+  float* ms;              // [n]
+  uint8_t* codes;         // kEncode/kEntryFused: out [n/2]; kUpdate: in
+  float* scales;          // kEncode/kEntryFused: out [n/128]; kUpdate: in
+  const float* e2;        // kUpdate: [own chunk], indexed from own_g0*128
+  uint32_t groups_work;   // virtual groups to process
+  uint32_t own_g0;        // own chunk, in groups
+  uint32_t own_g1;
+};
+
+template <int MODE, int U>
+__global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t half = (uint32_t)lane >> 5;
+  const uint32_t sub = (uint32_t)lane & 31u;
+  const uint32_t wave = (blockIdx.x * kBlock + threadIdx.x) >> 6;
+  const uint32_t nwaves = (gridDim.x * kBlock) >> 6;
+  const uint32_t nslices = (a.groups_work + 1u) >> 1;
+  const uint32_t own_len = a.own_g1 - a.own_g0;
+
+  for (uint32_t s0 = wave * U; s0 < nslices; s0 += nwaves * U) {
+    float xf[U][4], mf[U][4], ms[U][4];
+    uint32_t g[U];
+    bool ok[U];
+    uint32_t cw[U];
+    float sc[U];
+    float e2v[U][4];
+    bool own[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t v = 2u * (s0 + u) + half;
+      ok[u] = (s0 + u < nslices) && (v < a.groups_work);
+      uint32_t gg = v;
+      if (MODE == kEntryFused) gg = v < a.own_g0 ? v : v + own_len;
+      g[u] = ok[u] ? gg : 0u;
+      const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
+      uint2 xw = make_uint2(0u, 0u);
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f), s = make_float4(0.f, 0.f, 0.f, 0.f);
+      cw[u] = 0u;
+      sc[u] = 0.f;
+      e2v[u][0] = e2v[u][1] = e2v[u][2] = e2v[u][3] = 0.f;
+      own[u] = ok[u] && g[u] >= a.own_g0 && g[u] < a.own_g1;
+      if (ok[u]) {
+        xw = *reinterpret_cast<const uint2*>(a.x + e);
+        f = *reinterpret_cast<const float4*>(a.mf + e);
+        s = *reinterpret_cast<const float4*>(a.ms + e);
+        if (MODE == kUpdate) {
+          cw[u] = *reinterpret_cast<const uint16_t*>(a.codes + e / 2);
+          sc[u] = a.scales[g[u]];
+          if (own[u]) {
+            float4 t = *reinterpret_cast<const float4*>(a.e2 + (e - (int64_t)a.own_g0 * kGroup));
+            e2v[u][0] = t.x; e2v[u][1] = t.y; e2v[u][2] = t.z; e2v[u][3] = t.w;
+          }
+        }
+      }
+      unpack_bf16x4(xw, xf[u]);
+      mf[u][0] = f.x; mf[u][1] = f.y; mf[u][2] = f.z; mf[u][3] = f.w;
+      ms[u][0] = s.x; ms[u][1] = s.y; ms[u][2] = s.z; ms[u][3] = s.w;
+    }
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float xp[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) xp[k] = corrected(xf[u][k], mf[u][k], ms[u][k]);
+
+      float d1[4];
+      if (MODE == kUpdate) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) d1[k] = (float)nib(cw[u], k) * sc[u];
+      } else {
+        uint32_t m = max(max(abs_bits(xp[0]), abs_bits(xp[1])), max(abs_bits(xp[2]), abs_bits(xp[3])));
+        m = halfwave_max(m);
+        const float s = scale_of(m);
+        const float sd = code_divisor(s);
+        int q[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[k] = quant_code(xp[k], sd);
+        const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
+        if (ok[u]) {
+          *reinterpret_cast<uint16_t*>(a.codes + e / 2) = (uint16_t)pack_nib4(q);
+          if (sub == 0) a.scales[g[u]] = s;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) d1[k] = (float)q[k] * s;
+      }
+
+      if (MODE != kEncode) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float r = d1[k] - xp[k];
+          if (MODE == kUpdate && own[u]) r = r + e2v[u][k];  // e2 only on the own chunk
+          refresh(mf[u][k], ms[u][k], r);
+        }
+        if (ok[u]) {
+          const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
+          *reinterpret_cast<float4*>(a.mf + e) = make_float4(mf[u][0], mf[u][1], mf[u][2], mf[u][3]);
+          *reinterpret_cast<float4*>(a.ms + e) = make_float4(ms[u][0], ms[u][1], ms[u][2], ms[u][3]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// reduce kernel: rank-order sum of P stage-1 shards of one chunk, requantize
+
+enum ReduceMode { kShard = 0, kOwnFused = 1 };
+
+struct ReduceArgs {
+  const uint8_t* codes[kMaxRanks];   // shard q codes, chunk-local
+  const float* scales[kMaxRanks];    // shard q scales, chunk-local
+  uint8_t* out_codes;                // [chunk/2]
+  float* out_scales;                 // [chunk/128]
+  uint16_t* y;                       // [chunk] (nullable in kShard)
+  float* e2;                         // [chunk] (kShard, nullable)
+  const uint16_t* x;                 // kOwnFused: own chunk of x
+  float* mf;                         // kOwnFused: own chunk of the averages
+  float* ms;
+  uint32_t groups;                   // groups in the chunk
+  int32_t rank;                      // kOwnFused: the slot computed in registers
+};
+
+template <int MODE, int P, int U>
+__global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t half = (uint32_t)lane >> 5;
+  const uint32_t sub = (uint32_t)lane & 31u;
+  const uint32_t wave = (blockIdx.x * kBlock + threadIdx.x) >> 6;
+  const uint32_t nwaves = (gridDim.x * kBlock) >> 6;
+  const uint32_t nslices = (a.groups + 1u) >> 1;
+
+  for (uint32_t s0 = wave * U; s0 < nslices; s0 += nwaves * U) {
+    // issue every load of the U slices first
+    bool ok[U];
+    uint32_t g[U];
+    uint32_t cw[U][P];
+    float sc[U][P];
+    float xf[U][4], mf[U][4], ms[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t v = 2u * (s0 + u) + half;
+      ok[u] = (s0 + u < nslices) && (v < a.groups);
+      g[u] = ok[u] ? v : 0u;
+      const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        cw[u][q] = 0u;
+        sc[u][q] = 0.f;
+        if (ok[u] && !(MODE == kOwnFused && q == a.rank)) {
+          cw[u][q] = *reinterpret_cast<const uint16_t*>(a.codes[q] + e / 2);
+          sc[u][q] = a.scales[q][g[u]];
+        }
+      }
+      uint2 xw = make_uint2(0u, 0u);
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f), s = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (MODE == kOwnFused && ok[u]) {
+        xw = *reinterpret_cast<const uint2*>(a.x + e);
+        f = *reinterpret_cast<const float4*>(a.mf + e);
+        s = *reinterpret_cast<const float4*>(a.ms + e);
+      }
+      unpack_bf16x4(xw, xf[u]);
+      mf[u][0] = f.x; mf[u][1] = f.y; mf[u][2] = f.z; mf[u][3] = f.w;
+      ms[u][0] = s.x; ms[u][1] = s.y; ms[u][2] = s.z; ms[u][3] = s.w;
+    }
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
+      // own stage-1 quantization, in registers (same helpers as the entry pass)
+      float xp[4] = {0.f, 0.f, 0.f, 0.f}, d_own[4] = {0.f, 0.f, 0.f, 0.f};
+      if (MODE == kOwnFused) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xp[k] = corrected(xf[u][k], mf[u][k], ms[u][k]);
+        uint32_t m = max(max(abs_bits(xp[0]), abs_bits(xp[1])), max(abs_bits(xp[2]), abs_bits(xp[3])));
+        m = halfwave_max(m);
+        const float s1 = scale_of(m);
+        const float sd = code_divisor(s1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) d_own[k] = (float)quant_code(xp[k], sd) * s1;
+      }
+
+      // S = d_0 + d_1 + ... + d_{P-1}, in rank order
+      float S[4];
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float d;
+          if (MODE == kOwnFused && q == a.rank) d = d_own[k];
+          else d = (float)nib(cw[u][q], k) * sc[u][q];
+          S[k] = (q == 0) ? d : S[k] + d;
+        }
+      }
+
+      // stage-2 quantization
+      uint32_t m2 = max(max(abs_bits(S[0]), abs_bits(S[1])), max(abs_bits(S[2]), abs_bits(S[3])));
+      m2 = halfwave_max(m2);
+      const float s2 = scale_of(m2);
+      const float sd2 = code_divisor(s2);
+      int q2[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) q2[k] = quant_code(S[k], sd2);
+      const uint32_t y01 = pack_bf16x2((float)q2[0] * s2, (float)q2[1] * s2);
+      const uint32_t y23 = pack_bf16x2((float)q2[2] * s2, (float)q2[3] * s2);
+      float e2[4];
+      e2[0] = bf16_lo(y01) - S[0];
+      e2[1] = bf16_hi(y01) - S[1];
+      e2[2] = bf16_lo(y23) - S[2];
+      e2[3] = bf16_hi(y23) - S[3];
+
+      if (ok[u]) {
+        *reinterpret_cast<uint16_t*>(a.out_codes + e / 2) = (uint16_t)pack_nib4(q2);
+        if (sub == 0) a.out_scales[g[u]] = s2;
+        if (a.y) *reinterpret_cast<uint2*>(a.y + e) = make_uint2(y01, y23);
+        if (MODE == kShard && a.e2)
+          *reinterpret_cast<float4*>(a.e2 + e) = make_float4(e2[0], e2[1], e2[2], e2[3]);
+      }
+      if (MODE == kOwnFused) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float e1 = d_own[k] - xp[k];
+          refresh(mf[u][k], ms[u][k], e1 + e2[k]);
+        }
+        if (ok[u]) {
+          *reinterpret_cast<float4*>(a.mf + e) = make_float4(mf[u][0], mf[u][1], mf[u][2], mf[u][3]);
+          *reinterpret_cast<float4*>(a.ms + e) = make_float4(ms[u][0], ms[u][1], ms[u][2], ms[u][3]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// exit kernel: y = bf16(code * scale); blockIdx.y selects a segment
+
+struct DecodeSeg {
+  const uint8_t* codes;  // [groups*64]
+  const float* scales;   // [groups]
+  uint16_t* y;           // [groups*128]
+};
+
+struct DecodeArgs {
+  DecodeSeg seg[kMaxRanks];
+  uint32_t groups;  // groups per segment
+};
+
+template <int U>
+__global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t row = (uint32_t)lane >> 4;  // group within the wave's quad of groups
+  const uint32_t sub = (uint32_t)lane & 15u; // 8 elements each
+  const uint32_t wave = (blockIdx.x * kBlock + threadIdx.x) >> 6;
+  const uint32_t nwaves = (gridDim.x * kBlock) >> 6;
+  const uint32_t nquads = (a.groups + 3u) >> 2;
+  const DecodeSeg sg = a.seg[blockIdx.y];
+
+  for (uint32_t t0 = wave * U; t0 < nquads; t0 += nwaves * U) {
+    uint32_t cw[U];
+    float sc[U];
+    bool ok[U];
+    uint32_t g[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t v = 4u * (t0 + u) + row;
+      ok[u] = (t0 + u < nquads) && (v < a.groups);
+      g[u] = ok[u] ? v : 0u;
+      cw[u] = 0u;
+      sc[u] = 0.f;
+      if (ok[u]) {
+        cw[u] = *reinterpret_cast<const uint32_t*>(sg.codes + (int64_t)g[u] * (kGroup / 2) + sub * 4);
+        sc[u] = sg.scales[g[u]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint4 o;
+      o.x = pack_bf16x2((float)nib(cw[u], 0) * sc[u], (float)nib(cw[u], 1) * sc[u]);
+      o.y = pack_bf16x2((float)nib(cw[u], 2) * sc[u], (float)nib(cw[u], 3) * sc[u]);
+      o.z = pack_bf16x2((float)nib(cw[u], 4) * sc[u], (float)nib(cw[u], 5) * sc[u]);
+      o.w = pack_bf16x2((float)nib(cw[u], 6) * sc[u], (float)nib(cw[u], 7) * sc[u]);
+      if (ok[u]) *reinterpret_cast<uint4*>(sg.y + (int64_t)g[u] * kGroup + sub * 8) = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// zero fill (the averages start at zero); a kernel rather than a memset so
+// the call can sit inside a captured graph
+
+__global__ __launch_bounds__(kBlock) void k_zero2(float4* a, float4* b, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += stride) {
+    a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    b[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+}  // namespace echo

@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/echo.h declares, reports the same named parameters the oracle
+restates independently, and rejects bad arguments before launching anything
+(every call below fails validation, so no kernel is enqueued)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from error_compensated_bit_echo_amd import binding as B
+from oracle import oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "echo.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(echo_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for want in ("echo_state_init", "echo_encode", "echo_reduce_shard", "echo_decode",
+                 "echo_update", "echo_call", "echo_call_entry", "echo_call_reduce",
+                 "echo_call_exit", "echo_get_config", "echo_status_string", "echo_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    raw = C.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert set(declared_functions()) == set(B.EXPORTED)
+
+
+def test_config_matches_oracle_constants():
+    cfg = B.echo_get_config()
+    assert cfg["abi_version"] == B.echo_version() == 1
+    assert cfg["group"] == orc.GROUP == 128
+    assert cfg["qmax"] == orc.QMAX
+    assert cfg["max_ranks"] == orc.MAX_RANKS
+    assert cfg["w_fast"] == orc.W_FAST and cfg["w_slow"] == orc.W_SLOW
+    assert cfg["beta_fast"] == orc.BETA_FAST and cfg["alpha_fast"] == orc.ALPHA_FAST
+    assert cfg["beta_slow"] == orc.BETA_SLOW and cfg["alpha_slow"] == orc.ALPHA_SLOW
+    # the averages are normalized: B + A = 1, and the correction weights sum to 1
+    assert cfg["beta_fast"] + cfg["alpha_fast"] == 1.0
+    assert cfg["beta_slow"] + cfg["alpha_slow"] == 1.0
+    assert cfg["w_fast"] + cfg["w_slow"] == 1.0
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert B.status_string(code) and B.status_string(code) != "unknown status"
+    assert B.status_string(-99) == "unknown status"
+
+
+# Fake, well-aligned device addresses: never dereferenced, because every call
+# below is rejected by the host-side checks.
+A = 1 << 32
+
+
+def st(n=1024, P=2, rank=0, mf=A, ms=2 * A):
+    return B.EchoState(mf, ms, n, P, rank)
+
+
+def rc(fn, *args):
+    with pytest.raises(B.EchoError) as e:
+        fn(*args, stream=0)  # an explicit null stream: no GPU is touched
+    return e.value.status
+
+
+def test_state_init_rejections():
+    L = B.lib
+    s = B.EchoStateC()
+    assert L.echo_state_init(None, A, 2 * A, 1024, 2, 0, None) == -1
+    assert L.echo_state_init(C.byref(s), None, 2 * A, 1024, 2, 0, None) == -1
+    assert L.echo_state_init(C.byref(s), A, 2 * A, 1000, 2, 0, None) == -2
+    assert L.echo_state_init(C.byref(s), A, 2 * A, 0, 2, 0, None) == -2
+    assert L.echo_state_init(C.byref(s), A, 2 * A, 128, 2, 0, None) == -2   # n % (P*128)
+    assert L.echo_state_init(C.byref(s), A, 2 * A, 1024, 0, 0, None) == -4
+    assert L.echo_state_init(C.byref(s), A, 2 * A, 1024 * 17, 17, 0, None) == -4
+    assert L.echo_state_init(C.byref(s), A, 2 * A, 1024, 2, 2, None) == -4
+    assert L.echo_state_init(C.byref(s), A, 2 * A, 1024, 2, -1, None) == -4
+    assert L.echo_state_init(C.byref(s), A + 4, 2 * A, 1024, 2, 0, None) == -3
+    assert L.echo_state_init(C.byref(s), A, A + 1024, 1024, 2, 0, None) == -6  # overlap
+    assert L.echo_state_init(C.byref(s), A, 2 * A, (1 << 37) + 256, 2, 0, None) == -2
+
+
+def test_encode_rejections():
+    assert rc(B.echo_encode, st(), None, 3 * A, 4 * A) == -1
+    assert rc(B.echo_encode, st(), 3 * A + 2, 4 * A, 5 * A) == -3
+    assert rc(B.echo_encode, st(), 3 * A, 4 * A + 8, 5 * A) == -3
+    assert rc(B.echo_encode, st(), 3 * A, 4 * A, 5 * A + 2) == -3
+    assert rc(B.echo_encode, st(n=1000), 3 * A, 4 * A, 5 * A) == -2
+    assert rc(B.echo_encode, st(rank=5), 3 * A, 4 * A, 5 * A) == -4
+    # codes overlapping x, scales overlapping the averages
+    assert rc(B.echo_encode, st(), 3 * A, 3 * A + 16, 5 * A) == -6
+    assert rc(B.echo_encode, st(), 3 * A, 4 * A, A + 64) == -6
+
+
+def test_reduce_shard_rejections():
+    c = [3 * A, 4 * A]
+    s = [5 * A, 6 * A]
+    assert rc(B.echo_reduce_shard, c, s, 7 * A, 8 * A, None, None, 100) == -2
+    assert rc(B.echo_reduce_shard, [3 * A, None], s, 7 * A, 8 * A, None, None, 256) == -1
+    assert rc(B.echo_reduce_shard, [3 * A, 4 * A + 2], s, 7 * A, 8 * A, None, None, 256) == -3
+    assert rc(B.echo_reduce_shard, c, s, 7 * A, 8 * A, 9 * A + 2, None, 256) == -3
+    assert rc(B.echo_reduce_shard, c, s, 3 * A, 8 * A, None, None, 256) == -6  # out over shard
+    assert rc(B.echo_reduce_shard, c, s, 7 * A, 7 * A + 64, None, None, 256) == -6
+    assert rc(B.echo_reduce_shard, [3 * A] * 17, [5 * A] * 17, 7 * A, 8 * A, None, None, 256) == -4
+
+
+def test_decode_update_rejections():
+    assert rc(B.echo_decode, 3 * A, 4 * A, 5 * A, 100) == -2
+    assert rc(B.echo_decode, 3 * A, 4 * A, None, 128) == -1
+    assert rc(B.echo_decode, 3 * A, 4 * A, 3 * A, 128) == -6
+    assert rc(B.echo_update, st(), 3 * A, 4 * A, 5 * A, None) == -1
+    assert rc(B.echo_update, st(), 3 * A, 4 * A, 5 * A, 6 * A + 4) == -3
+    assert rc(B.echo_update, st(), A + 64, 4 * A, 5 * A, 6 * A) == -6  # x over m_fast
+
+
+def test_call_rejections():
+    P, n = 4, 4096
+    s4 = st(n=n, P=P, rank=1)
+    recv_c = [10 * A + k * A for k in range(P)]
+    recv_s = [20 * A + k * A for k in range(P)]
+    gath_c = [30 * A + k * A for k in range(P)]
+    gath_s = [40 * A + k * A for k in range(P)]
+    outs = [50 * A, 51 * A, 52 * A, 53 * A, 54 * A]
+    # slot `rank` may be NULL, the others may not
+    bad = list(recv_c)
+    bad[2] = None
+    assert rc(B.echo_call, s4, 3 * A, bad, recv_s, gath_c, gath_s, *outs) == -1
+    bad = list(gath_s)
+    bad[0] = 40 * A + 2
+    assert rc(B.echo_call, s4, 3 * A, recv_c, recv_s, gath_c, bad, *outs) == -3
+    # y may alias x exactly, but not partially; send may not overlap a gathered chunk
+    assert rc(B.echo_call, s4, 3 * A, recv_c, recv_s, gath_c, gath_s, 50 * A, 51 * A, 52 * A,
+              53 * A, 3 * A + 16) == -6
+    assert rc(B.echo_call, s4, 3 * A, recv_c, recv_s, gath_c, gath_s, 30 * A, 51 * A, 52 * A,
+              53 * A, 54 * A) == -6
+    assert rc(B.echo_call_reduce, s4, 3 * A, recv_c, recv_s, 52 * A, 53 * A, None) == -1
+    assert rc(B.echo_call_exit, s4, gath_c, gath_s, A) == -6  # y over m_fast
+    assert rc(B.echo_call_entry, st(n=n, P=P, rank=4), 3 * A, 50 * A, 51 * A) == -4
