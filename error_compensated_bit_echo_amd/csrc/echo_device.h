@@ -31,6 +31,32 @@ constexpr float kQmax = (float)ECHO_QMAX;
 constexpr int kMaxRanks = ECHO_MAX_RANKS;
 constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
 
+// Cache policy of the streaming accesses: every byte of the averages, the
+// input and the messages is touched once per call, so loads and stores of
+// the big streams may carry the non-temporal hint.
+#ifndef ECHO_NT_LOAD
+#define ECHO_NT_LOAD 1
+#endif
+#ifndef ECHO_NT_STORE
+#define ECHO_NT_STORE 1
+#endif
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+  if (ECHO_NT_LOAD) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_stream(T* p, T v) {
+  if (ECHO_NT_STORE) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // ---------------------------------------------------------------------------
 // lane-level helpers
 
@@ -144,8 +170,8 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
   const int lane = threadIdx.x & 63;
   const uint32_t half = (uint32_t)lane >> 5;
   const uint32_t sub = (uint32_t)lane & 31u;
-  const uint32_t wave = (blockIdx.x * kBlock + threadIdx.x) >> 6;
-  const uint32_t nwaves = (gridDim.x * kBlock) >> 6;
+  const uint32_t wave = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const uint32_t nwaves = gridDim.x * (kBlock / 64);
   const uint32_t nslices = (a.groups_work + 1u) >> 1;
   const uint32_t own_len = a.own_g1 - a.own_g0;
 
@@ -172,9 +198,12 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
       e2v[u][0] = e2v[u][1] = e2v[u][2] = e2v[u][3] = 0.f;
       own[u] = ok[u] && g[u] >= a.own_g0 && g[u] < a.own_g1;
       if (ok[u]) {
-        xw = *reinterpret_cast<const uint2*>(a.x + e);
-        f = *reinterpret_cast<const float4*>(a.mf + e);
-        s = *reinterpret_cast<const float4*>(a.ms + e);
+        const u32x2 xv = ld_stream(reinterpret_cast<const u32x2*>(a.x + e));
+        const f32x4 fv = ld_stream(reinterpret_cast<const f32x4*>(a.mf + e));
+        const f32x4 sv = ld_stream(reinterpret_cast<const f32x4*>(a.ms + e));
+        xw = make_uint2(xv.x, xv.y);
+        f = make_float4(fv.x, fv.y, fv.z, fv.w);
+        s = make_float4(sv.x, sv.y, sv.z, sv.w);
         if (MODE == kUpdate) {
           cw[u] = *reinterpret_cast<const uint16_t*>(a.codes + e / 2);
           sc[u] = a.scales[g[u]];
@@ -209,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
         for (int k = 0; k < 4; ++k) q[k] = quant_code(xp[k], sd);
         const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
         if (ok[u]) {
-          *reinterpret_cast<uint16_t*>(a.codes + e / 2) = (uint16_t)pack_nib4(q);
+          st_stream(reinterpret_cast<uint16_t*>(a.codes + e / 2), (uint16_t)pack_nib4(q));
           if (sub == 0) a.scales[g[u]] = s;
         }
 #pragma unroll
@@ -225,8 +254,8 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
         }
         if (ok[u]) {
           const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
-          *reinterpret_cast<float4*>(a.mf + e) = make_float4(mf[u][0], mf[u][1], mf[u][2], mf[u][3]);
-          *reinterpret_cast<float4*>(a.ms + e) = make_float4(ms[u][0], ms[u][1], ms[u][2], ms[u][3]);
+          st_stream(reinterpret_cast<f32x4*>(a.mf + e), f32x4{mf[u][0], mf[u][1], mf[u][2], mf[u][3]});
+          st_stream(reinterpret_cast<f32x4*>(a.ms + e), f32x4{ms[u][0], ms[u][1], ms[u][2], ms[u][3]});
         }
       }
     }
@@ -257,8 +286,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
   const int lane = threadIdx.x & 63;
   const uint32_t half = (uint32_t)lane >> 5;
   const uint32_t sub = (uint32_t)lane & 31u;
-  const uint32_t wave = (blockIdx.x * kBlock + threadIdx.x) >> 6;
-  const uint32_t nwaves = (gridDim.x * kBlock) >> 6;
+  const uint32_t wave = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const uint32_t nwaves = gridDim.x * (kBlock / 64);
   const uint32_t nslices = (a.groups + 1u) >> 1;
 
   for (uint32_t s0 = wave * U; s0 < nslices; s0 += nwaves * U) {
@@ -286,9 +315,12 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       uint2 xw = make_uint2(0u, 0u);
       float4 f = make_float4(0.f, 0.f, 0.f, 0.f), s = make_float4(0.f, 0.f, 0.f, 0.f);
       if (MODE == kOwnFused && ok[u]) {
-        xw = *reinterpret_cast<const uint2*>(a.x + e);
-        f = *reinterpret_cast<const float4*>(a.mf + e);
-        s = *reinterpret_cast<const float4*>(a.ms + e);
+        const u32x2 xv = ld_stream(reinterpret_cast<const u32x2*>(a.x + e));
+        const f32x4 fv = ld_stream(reinterpret_cast<const f32x4*>(a.mf + e));
+        const f32x4 sv = ld_stream(reinterpret_cast<const f32x4*>(a.ms + e));
+        xw = make_uint2(xv.x, xv.y);
+        f = make_float4(fv.x, fv.y, fv.z, fv.w);
+        s = make_float4(sv.x, sv.y, sv.z, sv.w);
       }
       unpack_bf16x4(xw, xf[u]);
       mf[u][0] = f.x; mf[u][1] = f.y; mf[u][2] = f.z; mf[u][3] = f.w;
@@ -343,7 +375,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       if (ok[u]) {
         *reinterpret_cast<uint16_t*>(a.out_codes + e / 2) = (uint16_t)pack_nib4(q2);
         if (sub == 0) a.out_scales[g[u]] = s2;
-        if (a.y) *reinterpret_cast<uint2*>(a.y + e) = make_uint2(y01, y23);
+        if (a.y) st_stream(reinterpret_cast<u32x2*>(a.y + e), u32x2{y01, y23});
         if (MODE == kShard && a.e2)
           *reinterpret_cast<float4*>(a.e2 + e) = make_float4(e2[0], e2[1], e2[2], e2[3]);
       }
@@ -354,8 +386,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
           refresh(mf[u][k], ms[u][k], e1 + e2[k]);
         }
         if (ok[u]) {
-          *reinterpret_cast<float4*>(a.mf + e) = make_float4(mf[u][0], mf[u][1], mf[u][2], mf[u][3]);
-          *reinterpret_cast<float4*>(a.ms + e) = make_float4(ms[u][0], ms[u][1], ms[u][2], ms[u][3]);
+          st_stream(reinterpret_cast<f32x4*>(a.mf + e), f32x4{mf[u][0], mf[u][1], mf[u][2], mf[u][3]});
+          st_stream(reinterpret_cast<f32x4*>(a.ms + e), f32x4{ms[u][0], ms[u][1], ms[u][2], ms[u][3]});
         }
       }
     }
@@ -381,8 +413,8 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const uint32_t row = (uint32_t)lane >> 4;  // group within the wave's quad of groups
   const uint32_t sub = (uint32_t)lane & 15u; // 8 elements each
-  const uint32_t wave = (blockIdx.x * kBlock + threadIdx.x) >> 6;
-  const uint32_t nwaves = (gridDim.x * kBlock) >> 6;
+  const uint32_t wave = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const uint32_t nwaves = gridDim.x * (kBlock / 64);
   const uint32_t nquads = (a.groups + 3u) >> 2;
   const DecodeSeg sg = a.seg[blockIdx.y];
 
@@ -410,7 +442,8 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
       o.y = pack_bf16x2((float)nib(cw[u], 2) * sc[u], (float)nib(cw[u], 3) * sc[u]);
       o.z = pack_bf16x2((float)nib(cw[u], 4) * sc[u], (float)nib(cw[u], 5) * sc[u]);
       o.w = pack_bf16x2((float)nib(cw[u], 6) * sc[u], (float)nib(cw[u], 7) * sc[u]);
-      if (ok[u]) *reinterpret_cast<uint4*>(sg.y + (int64_t)g[u] * kGroup + sub * 8) = o;
+      if (ok[u])
+        st_stream(reinterpret_cast<u32x4*>(sg.y + (int64_t)g[u] * kGroup + sub * 8), u32x4{o.x, o.y, o.z, o.w});
     }
   }
 }
