@@ -47,12 +47,23 @@ def step_bytes(N: int, P: int) -> float:
 
 
 def source_hash() -> str:
+    """Hash of the kernel and launch sources with comments and whitespace
+    removed (a comment edit does not change the kernels)."""
+    import re
+
     h = hashlib.sha256()
     for rel in ("error_compensated_bit_echo_amd/csrc/echo_device.h",
                 "error_compensated_bit_echo_amd/csrc/echo_api.hip",
                 "error_compensated_bit_echo_amd/build.py"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        if rel.endswith(".py"):
+            src = re.sub(r'""".*?"""', "", src, flags=re.S)
+            src = re.sub(r"#[^\n]*", "", src)
+        else:
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            src = re.sub(r"//[^\n]*", "", src)
+        h.update("".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -128,6 +139,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-log2n", type=int, default=26)
     ap.add_argument("--cpu-calls", type=int, default=24)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run a plain 1 GiB device copy (torch) before the warmup, as "
+                         "the known-size reference for HBM counter runs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -180,6 +194,14 @@ def main() -> int:
         if ev is not None:
             ev[3].record(stream)
 
+    if args.calibrate:
+        # a plain copy of known size: reads 1 GiB and writes 1 GiB
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"bench: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

@@ -5,10 +5,11 @@
  * Method: "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication for
  * LLM Training and Inference" (arXiv 2610.14277v1).  The all-reduce moves
  * 4-bit integers and sums in high precision, so every value is quantized at
- * most twice per call (fugumt page, abstract); a correction built from two
- * moving averages with different decay rates is added to the input before
- * each all-reduce, and the averages are refreshed from the output residual
- * (ai4snews page, "Interpretation").
+ * most twice per call ("Echo: Error-Compensated 4-Bit Tensor-Parallel
+ * Communication", Abstract); a correction built from two moving averages
+ * with different decay rates is added to the input before each all-reduce,
+ * and the averages are refreshed from the output residual ("Tensor-parallel
+ * traffic drops to 4 bits", Interpretation).
  *
  * One rank's view.  P ranks each hold an n-element bf16 tensor.  Chunk j is
  * the element range [j*n/P, (j+1)*n/P); rank j owns chunk j.  A call is:
@@ -111,8 +112,9 @@ typedef struct echo_config {
 int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int32_t nranks,
                     int32_t rank, echo_stream_t stream);
 
-/* Entry pass over all n elements (ai4snews "Interpretation": the correction
- * is added to the input before each all-reduce, fused into the entry pass):
+/* Entry pass over all n elements ("Tensor-parallel traffic drops to 4 bits",
+ * Interpretation: the correction is added to the input before each
+ * all-reduce, fused into the entry pass):
  * x' = f32(x) - (W_FAST*m_fast + W_SLOW*m_slow); per 128-group amax = max|x'|,
  * s = amax/7 (IEEE division), code = clamp(rint(x'/s), -7, 7); s == 0 gives
  * codes 0.  Writes codes[n/2] and scales[n/128]; reads the averages, does not
@@ -120,8 +122,9 @@ int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int
 int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* scales,
                 echo_stream_t stream);
 
-/* Reduce stage for one chunk of chunk_n elements (fugumt abstract: 4-bit
- * transport, high-precision sum, quantized at most twice): shard_codes /
+/* Reduce stage for one chunk of chunk_n elements ("Echo: Error-Compensated
+ * 4-Bit Tensor-Parallel Communication", Abstract: 4-bit transport,
+ * high-precision sum, quantized at most twice): shard_codes /
  * shard_scales are host arrays of nranks device pointers (shard q = rank q's
  * stage-1 message of this chunk: codes[chunk_n/2], scales[chunk_n/128]).
  * S = d_0 + d_1 + ... + d_{P-1} in binary32, in that order (d = code*scale);
@@ -138,8 +141,9 @@ int echo_reduce_shard(int32_t nranks, int64_t chunk_n, const uint8_t* const* sha
 int echo_decode(int64_t n, const uint8_t* codes, const float* scales, uint16_t* y,
                 echo_stream_t stream);
 
-/* Update (ai4snews "Interpretation": the averages are refreshed from the
- * output residual): with the pre-call averages, recompute x' as the entry
+/* Update ("Tensor-parallel traffic drops to 4 bits", Interpretation: the
+ * averages are refreshed from the output residual): with the pre-call
+ * averages, recompute x' as the entry
  * pass does, d1 = code1*scale1, r = d1 - x' plus e2_own[i - rank*n/P] on the
  * own chunk; then m_fast <- B_FAST*m_fast + A_FAST*r, m_slow <- B_SLOW*m_slow +
  * A_SLOW*r in place.  codes1/scales1 are this rank's entry-pass output for

@@ -6,17 +6,19 @@
  * CPU-baseline leg of the benchmark, never by the product path.  It shares
  * no code with the HIP library.
  *
- * What the method computes, per the pages (arXiv 2610.14277v1; the ai4snews
- * summary, section "Interpretation"; the abstract on the fugumt page):
+ * What the method computes, per the pages (arXiv 2610.14277v1).  Pages:
+ * "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication" (EC),
+ * "Tensor-parallel traffic drops to 4 bits" (TP), "How Echo lets big AI
+ * models train faster" (HE).
  *   - the all-reduce payload travels as 4-bit integers and is summed in
- *     high precision (ai4snews "Interpretation"; fugumt abstract);
+ *     high precision (TP, Interpretation; EC, Abstract);
  *   - each value is quantized at most twice per call for any number of GPUs
- *     (fugumt abstract; heraldofai "How Echo keeps errors from snowballing");
+ *     (EC, Abstract; HE, "How Echo keeps errors from snowballing");
  *   - a correction built from two moving averages with different decay
  *     rates is added to the input before each all-reduce, and the averages
- *     are refreshed from the output residual (ai4snews "Interpretation");
+ *     are refreshed from the output residual (TP, Interpretation);
  *   - the sum reveals the error the call injected and feeding it back makes
- *     old errors cancel (fugumt abstract).
+ *     old errors cancel (EC, Abstract).
  * Every detail the pages leave open (group size, scale type, code range,
  * rounding, nibble order, decays, how the averages combine, the residual's
  * exact definition) follows the stated readings: see echo_oracle.h.

@@ -8,8 +8,9 @@
  * and a test checks that the library reports the same values.
  *
  * Source: "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication for
- * LLM Training and Inference" (arXiv 2610.14277v1), as summarised on the
- * ai4snews page ("Interpretation") and in the abstract on the fugumt page.
+ * LLM Training and Inference" (arXiv 2610.14277v1): its Abstract, and the
+ * summary page "Tensor-parallel traffic drops to 4 bits", section
+ * Interpretation.
  *
  * Arithmetic: IEEE binary32, round-to-nearest-even, one rounding per
  * operation, no contraction (built with -ffp-contract=off), denormals kept.

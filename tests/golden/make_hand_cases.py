@@ -4,7 +4,7 @@ The expected values here are derived by hand (see each case's "why"); this
 script only lays them out, with every float stored as float.hex() so the
 fixture is exact.  It imports nothing from the library or the oracle.
 Sources: the pages fix "4-bit integer transport" with per-group scaling
-(ai4snews "Interpretation"; fugumt abstract); the group size 128, the code
+("Tensor-parallel traffic drops to 4 bits", Interpretation; "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication", Abstract); the group size 128, the code
 range [-7, 7], s = amax / 7 and round-half-to-even are the stated readings.
 """
 import json
@@ -75,7 +75,8 @@ BF16 = [
 def main():
     out = dict(
         source="hand-derived; readings of the pages' 4-bit group quantization "
-               "(ai4snews 'Interpretation', fugumt abstract)",
+               "('Tensor-parallel traffic drops to 4 bits', Interpretation; "
+               "'Echo: Error-Compensated 4-Bit Tensor-Parallel Communication', Abstract)",
         quantizer=[dict(name=c["name"], why=c["why"], v=[float(t).hex() for t in c["v"]],
                         scale=float(c["scale"]).hex(), codes=c["codes"]) for c in CASES],
         pack=PACK, bf16=BF16)

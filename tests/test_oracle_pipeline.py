@@ -1,15 +1,17 @@
 """Pins of the oracle's whole pipeline (CPU only).
 
-What the pages fix and how each is checked:
+Pages: "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication" (EC),
+"Tensor-parallel traffic drops to 4 bits" (TP), "How Echo lets big AI models
+train faster" (HE).  What they fix and how each is checked:
   * each value is quantized at most twice per call for any number of GPUs
-    (fugumt abstract; heraldofai "How Echo keeps errors from snowballing"):
+    (EC, Abstract; HE, "How Echo keeps errors from snowballing"):
     instrumented counts, and a ring all-reduce that requantizes at every
     hop as the contrast whose error grows with P;
   * the sum is formed in high precision and reveals the injected error,
-    which is fed back (ai4snews "Interpretation"; fugumt abstract): the
-    residual identity sum_p r_p = y - sum_p x'_p;
-  * the accumulated error stays bounded independently of depth (fugumt
-    abstract; ai4snews "Perspective"): the deep-chain test, compensated vs
+    which is fed back (TP, Interpretation; EC, Abstract): the residual
+    identity sum_p r_p = y - sum_p x'_p;
+  * the accumulated error stays bounded independently of depth (EC,
+    Abstract; TP, Perspective): the deep-chain test, compensated vs
     uncompensated;
   * exact-arithmetic re-derivation of a whole call on tiny inputs, and
     symmetries (power-of-two scaling, negation, P = 1 idempotence).

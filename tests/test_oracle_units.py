@@ -1,8 +1,10 @@
 """Pins of the oracle's building blocks against hand-derived values, exact
 arithmetic and library routines (CPU only).
 
-The pages fix 4-bit integer transport with a high-precision sum (ai4snews
-"Interpretation"; fugumt abstract); the group size, code range, scale rule,
+The pages fix 4-bit integer transport with a high-precision sum
+("Tensor-parallel traffic drops to 4 bits", Interpretation; "Echo:
+Error-Compensated 4-Bit Tensor-Parallel Communication", Abstract); the group
+size, code range, scale rule,
 rounding and nibble order are the stated readings, checked here by values
 worked out by hand (tests/golden/quantizer_hand_cases.json) and by exact
 rational re-derivation.
