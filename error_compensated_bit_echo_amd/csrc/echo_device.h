@@ -42,6 +42,24 @@ constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
 #define ECHO_NT_STORE 1
 #endif
 
+// Workgroups are dealt to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8), and each XCD has its own L2.  Renumbering them so that each XCD
+// takes one contiguous run of tiles keeps lines shared by neighbouring tiles
+// (the per-group scales: 8 bytes per wavefront) inside one L2.
+#ifndef ECHO_XCD_REMAP
+#define ECHO_XCD_REMAP 1
+#endif
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t tile_index() {
+  const uint32_t b = blockIdx.x;
+  if (!ECHO_XCD_REMAP) return b;
+  const uint32_t nb = gridDim.x;
+  const uint32_t xcd = b % kXcds, k = b / kXcds;
+  const uint32_t per = nb / kXcds, extra = nb % kXcds;
+  return xcd * per + (xcd < extra ? xcd : extra) + k;
+}
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -171,7 +189,7 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
   const int lane = threadIdx.x & 63;
   const uint32_t half = (uint32_t)lane >> 5;
   const uint32_t sub = (uint32_t)lane & 31u;
-  const uint32_t wave = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const uint32_t wave = tile_index() * (kBlock / 64) + (threadIdx.x >> 6);
   const uint32_t nwaves = gridDim.x * (kBlock / 64);
   const uint32_t nslices = (a.groups_work + 1u) >> 1;
   const uint32_t own_len = a.own_g1 - a.own_g0;
@@ -287,7 +305,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
   const int lane = threadIdx.x & 63;
   const uint32_t half = (uint32_t)lane >> 5;
   const uint32_t sub = (uint32_t)lane & 31u;
-  const uint32_t wave = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const uint32_t wave = tile_index() * (kBlock / 64) + (threadIdx.x >> 6);
   const uint32_t nwaves = gridDim.x * (kBlock / 64);
   const uint32_t nslices = (a.groups + 1u) >> 1;
 
@@ -414,7 +432,8 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const uint32_t row = (uint32_t)lane >> 4;  // group within the wave's quad of groups
   const uint32_t sub = (uint32_t)lane & 15u; // 8 elements each
-  const uint32_t wave = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const uint32_t wave = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);  // measured: the exit
+  // pass streams faster without the XCD renumbering
   const uint32_t nwaves = gridDim.x * (kBlock / 64);
   const uint32_t nquads = (a.groups + 3u) >> 2;
   const DecodeSeg sg = a.seg[blockIdx.y];

@@ -200,3 +200,47 @@ def int4_message(n: int, key: int, scale_lo: float = 0.05, scale_hi: float = 0.5
         cv = codes.reshape(g, group // 2)
         cv[zg] = 0
     return codes, scales
+
+
+# ---- device-side recipes (torch's seeded Philox generator on the GPU) ------------
+# For call sequences too long to draw on the host (the training workload's 112
+# calls of 32M elements).  Deterministic for a given seed, shape and device;
+# both sides of a comparison read the same device bytes.
+
+def _device_gen(seed: int, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) & ((1 << 63) - 1))
+    return g
+
+
+def device_lognormal_channel_activations(tokens: int, hidden: int, seed: int, lam, device,
+                                         sigma: float = 0.5):
+    """bf16 bits (int16 tensor) of sigma * z * lam[c]; lam is the per-channel
+    scale (outliers included) from channel_scales()."""
+    import torch
+
+    g = _device_gen(seed, device)
+    z = torch.randn(tokens, hidden, generator=g, device=device)
+    lam_t = torch.as_tensor(lam, dtype=torch.float32, device=device)
+    return (sigma * z * lam_t[None, :]).to(torch.bfloat16).view(torch.int16).reshape(-1)
+
+
+def device_student_t3(n: int, seed: int, device, scale: float = 1e-3):
+    """bf16 bits (int16 tensor) of scale * z / sqrt((z1^2 + z2^2 + z3^2) / 3)."""
+    import torch
+
+    g = _device_gen(seed, device)
+    z = torch.randn(4, n, generator=g, device=device)
+    t = z[0] / torch.sqrt((z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3.0)
+    return (scale * t).to(torch.bfloat16).view(torch.int16)
+
+
+def channel_scales(hidden: int, channel_key: int, channel_sigma: float = 1.0,
+                   outlier_mult: float = 30.0, outlier_frac: float = 0.001) -> np.ndarray:
+    """Per-channel scale exp(N(0, channel_sigma)), a fixed 0.1% subset x mult
+    (the same lambda as lognormal_channel_activations)."""
+    lam = np.exp(channel_sigma * normal(hidden, stream_key(channel_key, "lambda")))
+    lam[outlier_channels(hidden, outlier_frac, stream_key(channel_key, "outliers"))] *= outlier_mult
+    return lam.astype(np.float32)

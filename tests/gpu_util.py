@@ -11,6 +11,18 @@ from error_compensated_bit_echo_amd import binding as B
 DEV = "cuda:0"
 
 
+def eq(a, b, what):
+    """bitwise equality of two arrays, with the first mismatches in the message"""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert a.shape == b.shape, (what, a.shape, b.shape)
+    if a.dtype == np.float32:
+        a, b = a.view(np.uint32), b.view(np.uint32)
+    bad = np.nonzero(a.ravel() != b.ravel())[0]
+    assert bad.size == 0, (f"{what}: {bad.size} mismatches, first at {bad[:5]}: "
+                           f"{a.ravel()[bad[:5]]} vs {b.ravel()[bad[:5]]}")
+
+
 def dev(a: np.ndarray) -> torch.Tensor:
     """numpy array -> device tensor holding the same bytes."""
     a = np.ascontiguousarray(a)
@@ -91,3 +103,6 @@ def gpu_simulate_call(ranks, xs_np):
                     own2[p], own2s[p], r.y)
     torch.cuda.synchronize()
     return codes2, scales2, own2, own2s
+
+
+from windows import WindowOracle, pick_windows  # noqa: E402,F401

@@ -1,0 +1,242 @@
+"""GPU parity at the full sizes of the five workloads, through the C ABI, in
+the launch configuration bench.py times.
+
+  tiny     P=8 ranks simulated on one GPU, bf16 [16 x 4096] per rank, 4 calls
+           from zero state: every output of every rank against the oracle's
+           full simulation.
+  decode   P=8 simulated, [256 x 4096] per rank, 64 calls with the averages
+           carried: every output, every call.
+  prefill  rank mode, [8192 x 4096] (32M elements), 4 warm-up calls then the
+           measured call; sampled windows of every chunk checked after every
+           call (the oracle follows each window through the whole sequence),
+           the exit pass checked in full.
+  train    rank mode, [8 x 4096 x 1024], 56 forward calls on one state then 56
+           backward calls on another, inputs drawn on the GPU each call;
+           sampled windows after every call.
+  1gb      rank mode, bf16[2^29], 23 calls on the same input (the bench's 3
+           warm-up + 20 timed); sampled windows after every call, the first
+           call's whole send message and the whole exit pass checked in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as g
+from error_compensated_bit_echo_amd import binding as B
+from error_compensated_bit_echo_amd import inputs as I
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ---- full simulation ------------------------------------------------------------------
+
+def _simulate_sequence(P, n, calls, make_x, label):
+    mf = [np.zeros(n, np.float32) for _ in range(P)]
+    ms = [np.zeros(n, np.float32) for _ in range(P)]
+    ranks = [g.GpuRank(np.zeros(n, np.uint16), mf[p], ms[p], P, p) for p in range(P)]
+    for call in range(calls):
+        xs = [make_x(call, p) for p in range(P)]
+        codes2, scales2, _, _ = g.gpu_simulate_call(ranks, xs)
+        want = orc.simulate(xs, mf, ms)
+        g.eq(g.host(codes2, np.uint8), want["codes2"], f"{label} call {call} codes2")
+        g.eq(g.host(scales2, np.float32), want["scales2"], f"{label} call {call} scales2")
+        for p, r in enumerate(ranks):
+            g.eq(g.host(r.y, np.uint16), want["y"], f"{label} call {call} y rank {p}")
+            g.eq(g.host(r.mf, np.float32), mf[p], f"{label} call {call} m_fast rank {p}")
+            g.eq(g.host(r.ms, np.float32), ms[p], f"{label} call {call} m_slow rank {p}")
+        if call % 16 == 0:
+            say(f"{label}: call {call} ok")
+
+
+def test_config_tiny_full_simulation():
+    P, tokens, hidden = 8, 16, 4096
+    ck = I.stream_key("tiny", 0, "channels")
+
+    def make_x(call, p):
+        return I.gaussian_outlier_channels(tokens, hidden, I.stream_key("tiny", 0, call, p),
+                                           outlier_mult=20.0, channel_key=ck)
+    _simulate_sequence(P, tokens * hidden, 4, make_x, "tiny")
+
+
+@pytest.mark.timeout(600)
+def test_config_decode_full_simulation():
+    P, tokens, hidden = 8, 256, 4096
+    ck = I.stream_key("decode", 0, "channels")
+
+    def make_x(call, p):
+        return I.lognormal_channel_activations(tokens, hidden, I.stream_key("decode", 0, call, p), ck)
+    _simulate_sequence(P, tokens * hidden, 64, make_x, "decode")
+
+
+# ---- rank mode --------------------------------------------------------------------------
+
+class RankRun:
+    """Device buffers of one rank-mode sequence plus the oracle's windows."""
+
+    def __init__(self, P, rank, n, seed, windows_per_chunk=2, W=4, label=""):
+        self.P, self.rank, self.n, self.C = P, rank, n, n // P
+        self.label = label
+        C = self.C
+        self.recv = [None if q == rank else I.int4_message(C, I.stream_key(label, seed, "recv", q),
+                                                           zero_group_frac=1e-3)
+                     for q in range(P)]
+        self.gath = [None if j == rank else
+                     I.int4_message(C, I.stream_key(label, seed, "gath", j), scale_lo=0.15,
+                                    scale_hi=1.5, zero_group_frac=1e-3)
+                     for j in range(P)]
+        self.recv_d = [None if m is None else (g.dev(m[0]), g.dev(m[1])) for m in self.recv]
+        self.gath_d = [None if m is None else (g.dev(m[0]), g.dev(m[1])) for m in self.gath]
+        self.mf = g.empty_f32(n)
+        self.ms = g.empty_f32(n)
+        self.st = B.echo_state_init(self.mf, self.ms, n, P, rank)
+        self.send_c = g.empty_u8(n // 2)
+        self.send_s = g.empty_f32(n // 128)
+        self.own_c = g.empty_u8(C // 2)
+        self.own_s = g.empty_f32(C // 128)
+        self.y = g.empty_bf16(n)
+        rng = np.random.default_rng(seed)
+        self.wins = [g.WindowOracle(P, rank, j, off, W)
+                     for j, off in g.pick_windows(P, C, W, rng, windows_per_chunk)]
+
+    def call(self, xd):
+        sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
+        B.echo_call(self.st, xd, sl(self.recv_d, 0), sl(self.recv_d, 1), sl(self.gath_d, 0),
+                    sl(self.gath_d, 1), self.send_c, self.send_s, self.own_c, self.own_s, self.y)
+
+    def check_windows(self, xd, tag):
+        """Run every window's oracle one call further and compare."""
+        torch.cuda.synchronize()
+        C, r = self.C, self.rank
+        for w in self.wins:
+            es = w.elems(C)
+            ce = w.chunk_elems()
+            x_win = g.host(xd[es], np.uint16)
+            if w.j == r:
+                msg = [None if q == r else (self.recv[q][0][ce.start // 2:ce.stop // 2],
+                                            self.recv[q][1][ce.start // 128:ce.stop // 128])
+                       for q in range(self.P)]
+            else:
+                m = self.gath[w.j]
+                msg = (m[0][ce.start // 2:ce.stop // 2], m[1][ce.start // 128:ce.stop // 128])
+            want = w.call(x_win, msg)
+            what = f"{self.label} {tag} window (chunk {w.j}, group {w.off})"
+            g.eq(g.host(self.y[es], np.uint16), want["y"], what + " y")
+            g.eq(g.host(self.mf[es], np.float32), want["m_fast"], what + " m_fast")
+            g.eq(g.host(self.ms[es], np.float32), want["m_slow"], what + " m_slow")
+            if w.j == r:
+                g.eq(g.host(self.own_c[ce.start // 2:ce.stop // 2], np.uint8), want["codes"], what + " codes2")
+                g.eq(g.host(self.own_s[ce.start // 128:ce.stop // 128], np.float32), want["scales"],
+                     what + " scales2")
+            else:
+                g.eq(g.host(self.send_c[es.start // 2:es.stop // 2], np.uint8), want["codes"], what + " send codes")
+                g.eq(g.host(self.send_s[es.start // 128:es.stop // 128], np.float32), want["scales"],
+                     what + " send scales")
+
+    def check_exit_full(self, tag):
+        """The whole exit pass: y on every non-own chunk against the oracle's
+        decode of the gathered chunk; the own chunk's y against the decode of
+        the own stage-2 chunk."""
+        torch.cuda.synchronize()
+        C, r = self.C, self.rank
+        y = g.host(self.y, np.uint16)
+        for j in range(self.P):
+            want = (orc.decode(g.host(self.own_c, np.uint8), g.host(self.own_s, np.float32), C)
+                    if j == r else orc.decode(self.gath[j][0], self.gath[j][1], C))
+            g.eq(y[j * C:(j + 1) * C], want, f"{self.label} {tag} y chunk {j}")
+
+    def check_message_properties(self, tag):
+        """Send and own stage-2 messages never hold the code -8 and their scales
+        are finite and non-negative."""
+        torch.cuda.synchronize()
+        C, r = self.C, self.rank
+        sc = g.host(self.send_c, np.uint8)
+        ss = g.host(self.send_s, np.float32)
+        keep = np.ones(self.n // 2, bool)
+        keep[r * C // 2:(r + 1) * C // 2] = False
+        keep_s = np.ones(self.n // 128, bool)
+        keep_s[r * C // 128:(r + 1) * C // 128] = False
+        for codes, scales in ((sc[keep], ss[keep_s]),
+                              (g.host(self.own_c, np.uint8), g.host(self.own_s, np.float32))):
+            assert not np.any((codes & 0xF) == 8) and not np.any((codes >> 4) == 8), tag
+            assert np.all(np.isfinite(scales)) and np.all(scales >= 0), tag
+
+
+@pytest.mark.timeout(600)
+def test_config_prefill_rank_mode():
+    P, rank, tokens, hidden = 8, 0, 8192, 4096
+    n = tokens * hidden
+    run = RankRun(P, rank, n, seed=3, label="prefill")
+    ck = I.stream_key("prefill", "channels")
+    for call in range(5):  # 4 warm-up calls, then the measured call on warm state
+        x = I.lognormal_channel_activations(tokens, hidden, I.stream_key("prefill", call), ck)
+        xd = g.dev(x)
+        run.call(xd)
+        run.check_windows(xd, f"call {call}")
+        say(f"prefill: call {call} windows ok")
+    run.check_exit_full("final call")
+    run.check_message_properties("final call")
+
+
+@pytest.mark.timeout(900)
+def test_config_train_rank_mode():
+    """56 forward calls (activations) on one state, then 56 backward calls
+    (1e-3 Student-t(3) gradients) in reverse site order on another."""
+    P, rank = 8, 5
+    b, s, hidden = 8, 4096, 1024
+    n = b * s * hidden
+    dev = torch.device(g.DEV)
+    lam = I.channel_scales(hidden, I.stream_key("train", "channels"))
+    fwd = RankRun(P, rank, n, seed=41, windows_per_chunk=1, label="train-fwd")
+    bwd = RankRun(P, rank, n, seed=43, windows_per_chunk=1, label="train-bwd")
+    for site in range(56):
+        xd = I.device_lognormal_channel_activations(b * s, hidden, 1000 + site, lam, dev)
+        fwd.call(xd)
+        fwd.check_windows(xd, f"forward site {site}")
+        if site % 14 == 0:
+            say(f"train: forward site {site} ok")
+    for site in reversed(range(56)):
+        xd = I.device_student_t3(n, 2000 + site, dev)
+        bwd.call(xd)
+        bwd.check_windows(xd, f"backward site {site}")
+        if site % 14 == 0:
+            say(f"train: backward site {site} ok")
+    fwd.check_message_properties("last forward call")
+    bwd.check_message_properties("last backward call")
+    bwd.check_exit_full("last backward call")
+
+
+@pytest.mark.timeout(900)
+def test_config_1gb_rank_mode():
+    """The bench's workload and call sequence: bf16[2^29], P = 8, rank 0,
+    3 warm-up + 20 timed calls on the same input, the averages carried."""
+    P, rank, n = 8, 0, 1 << 29
+    C = n // P
+    say("1gb: generating inputs")
+    x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 0, "x"), outlier_mult=20.0)
+    xd = g.dev(x)
+    run = RankRun(P, rank, n, seed=0, windows_per_chunk=3, label="1gb")
+    for call in range(23):
+        run.call(xd)
+        if call == 0:
+            # whole send message of the first call (zero state) against the oracle
+            torch.cuda.synchronize()
+            zeros = np.zeros(C, np.float32)
+            sc = g.host(run.send_c, np.uint8)
+            ss = g.host(run.send_s, np.float32)
+            for j in range(P):
+                if j == rank:
+                    continue
+                wc, ws = orc.encode(np.ascontiguousarray(x[j * C:(j + 1) * C]), zeros, zeros)
+                g.eq(sc[j * C // 2:(j + 1) * C // 2], wc, f"1gb call 0 send codes chunk {j}")
+                g.eq(ss[j * C // 128:(j + 1) * C // 128], ws, f"1gb call 0 send scales chunk {j}")
+            say("1gb: call 0 whole send message ok")
+        run.check_windows(xd, f"call {call}")
+        if call % 5 == 0:
+            say(f"1gb: call {call} windows ok")
+    run.check_exit_full("call 22")
+    run.check_message_properties("call 22")
