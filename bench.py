@@ -129,6 +129,118 @@ def cpu_baseline(x, recv, gath, P: int, rank: int, n_sample: int, calls: int):
     }
 
 
+def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, y, e2,
+              N, P, rank, steps):
+    """The compensation's cost on the critical path (the pages' schedule runs
+    the averages' update beside the next matrix multiplication).  Times, per
+    call: the fused call; the uncompensated call; the split schedule's
+    critical path (entry pass with the averages read-only, reduce, exit)
+    with the update on a side stream; and each followed by a matmul that
+    consumes y -- one TP=8 shard of a Llama-3-8B MLP up-projection,
+    [N/4096 x 4096] @ [4096 x 1792] in bf16."""
+    C = N // P
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    w = torch.randn(4096, 1792, device=y.device, dtype=torch.bfloat16) * 0.02
+    yb = y.view(torch.bfloat16).reshape(-1, 4096)
+    sh_c = [send_c[rank * C // 2:(rank + 1) * C // 2] if q == rank else rc_[q] for q in range(P)]
+    sh_s = [send_s[rank * C // 128:(rank + 1) * C // 128] if q == rank else rs_[q] for q in range(P)]
+
+    def fused():
+        B.echo_call(st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, y, main)
+
+    def plain():
+        B.echo_call_plain(P, rank, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, y,
+                          stream=main)
+
+    state = {"updated": None}
+
+    def split_critical():
+        if state["updated"] is not None:
+            main.wait_event(state["updated"])
+        B.echo_encode(st, xd, send_c, send_s, main)
+        B.echo_reduce_shard(sh_c, sh_s, own_c, own_s, y[rank * C:(rank + 1) * C], e2, chunk_n=C,
+                            stream=main)
+        reduced = torch.cuda.Event()
+        reduced.record(main)
+        B.echo_call_exit(st, gc_, gs_, y, main)
+        return reduced
+
+    def split_update(reduced):
+        side.wait_event(reduced)
+        B.echo_update(st, xd, send_c, send_s, e2, side)
+        ev = torch.cuda.Event()
+        ev.record(side)
+        state["updated"] = ev
+
+    def gemm():
+        return yb @ w
+
+    def timed(body, k=steps):
+        body()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(k)]
+        t0 = time.perf_counter()
+        for e in evs:
+            body(e)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / k
+        first = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        return wall, first
+
+    import numpy as np
+
+    def b_fused(e=None):
+        if e: e[0].record(main)
+        fused()
+        if e: e[1].record(main)
+        gemm()
+
+    def b_plain(e=None):
+        if e: e[0].record(main)
+        plain()
+        if e: e[1].record(main)
+        gemm()
+
+    def b_split(e=None):
+        if e: e[0].record(main)
+        reduced = split_critical()
+        if e: e[1].record(main)
+        gemm()
+        split_update(reduced)
+
+    def b_gemm(e=None):
+        if e: e[0].record(main)
+        gemm()
+        if e: e[1].record(main)
+
+    def b_update(e=None):
+        if e: e[0].record(main)
+        B.echo_update(st, xd, send_c, send_s, e2, main)
+        if e: e[1].record(main)
+
+    out = {}
+    for name, body in (("gemm", b_gemm), ("fused", b_fused), ("plain", b_plain), ("split", b_split),
+                       ("update_alone", b_update)):
+        wall, first = timed(body)
+        out[name] = (wall, first)
+    torch.cuda.synchronize()
+    return {
+        "matmul": "[%d x 4096] @ [4096 x 1792] bf16" % (N // 4096),
+        "matmul_ms": round(out["gemm"][1], 4),
+        "fused_call_ms": round(out["fused"][1], 4),
+        "plain_call_ms": round(out["plain"][1], 4),
+        "split_critical_ms": round(out["split"][1], 4),
+        "update_alone_ms": round(out["update_alone"][1], 4),
+        "layer_ms": {"fused+matmul": round(out["fused"][0], 4), "plain+matmul": round(out["plain"][0], 4),
+                     "split+matmul(update beside it)": round(out["split"][0], 4)},
+        "compensation_on_critical_path_ms": {
+            "fused": round(out["fused"][1] - out["plain"][1], 4),
+            "split": round(out["split"][1] - out["plain"][1], 4)},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +251,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-log2n", type=int, default=26)
     ap.add_argument("--cpu-calls", type=int, default=24)
+    ap.add_argument("--no-schedules", action="store_true",
+                    help="skip the critical-path comparison (fused / split / uncompensated)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) before the warmup, as "
                          "the known-size reference for HBM counter runs")
@@ -264,6 +378,11 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    if not args.no_schedules:
+        print("bench: critical-path schedules", file=sys.stderr, flush=True)
+        e2 = torch.empty(C, dtype=torch.float32, device=dev)
+        out["schedules"] = schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c,
+                                     own_s, y, e2, N, P, rank, args.steps)
     if not args.no_cpu:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         n_s = min(N, 1 << args.cpu_log2n)

@@ -52,6 +52,8 @@ _SIGNATURES = {
     "echo_call_reduce": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp, _vp, _vp],
     "echo_call_exit": [C.POINTER(EchoStateC), _pp, _pp, _vp, _vp],
     "echo_call": [C.POINTER(EchoStateC), _vp, _pp, _pp, _pp, _pp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "echo_call_plain": [C.c_int32, C.c_int32, C.c_int64, _vp, _pp, _pp, _pp, _pp, _vp, _vp, _vp,
+                        _vp, _vp, _vp],
     "echo_get_config": [C.POINTER(EchoConfigC)],
     "echo_status_string": [C.c_int],
     "echo_version": [],
@@ -184,6 +186,17 @@ def echo_call(st: EchoState, x, recv_codes, recv_scales, gath_codes, gath_scales
                          _ptrs(gath_codes), _ptrs(gath_scales), _ptr(send_codes),
                          _ptr(send_scales), _ptr(own_codes2), _ptr(own_scales2), _ptr(y),
                          _stream(stream)), "echo_call")
+
+
+def echo_call_plain(nranks, rank, x, recv_codes, recv_scales, gath_codes, gath_scales,
+                    send_codes, send_scales, own_codes2, own_scales2, y, n=None,
+                    stream=None) -> None:
+    if n is None:
+        n = x.numel()
+    _check(lib.echo_call_plain(int(nranks), int(rank), int(n), _ptr(x), _ptrs(recv_codes),
+                               _ptrs(recv_scales), _ptrs(gath_codes), _ptrs(gath_scales),
+                               _ptr(send_codes), _ptr(send_scales), _ptr(own_codes2),
+                               _ptr(own_scales2), _ptr(y), _stream(stream)), "echo_call_plain")
 
 
 def echo_get_config() -> dict:

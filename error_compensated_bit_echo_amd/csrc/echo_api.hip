@@ -242,6 +242,42 @@ int run_exit(const echo_state* st, const uint8_t* const* gath_codes,
   return launch_decode(a, k, s);
 }
 
+// ---- the uncompensated call: x' = f32(x), no averages ----------------------
+
+int run_entry_plain(const echo_state* geo, const uint16_t* x, uint8_t* send_codes,
+                    float* send_scales, hipStream_t s) {
+  const Geometry g = geometry(geo);
+  Stage1Args a;
+  memset(&a, 0, sizeof a);
+  a.x = x;
+  a.codes = send_codes;
+  a.scales = send_scales;
+  a.groups_work = g.groups - g.chunk_groups;
+  a.own_g0 = g.own_g0;
+  a.own_g1 = g.own_g1;
+  return launch_stage1<kEntryPlain>(a, s);
+}
+
+int run_reduce_plain(const echo_state* geo, const uint16_t* x, const uint8_t* const* recv_codes,
+                     const float* const* recv_scales, uint8_t* own_codes2, float* own_scales2,
+                     uint16_t* y, hipStream_t s) {
+  const Geometry g = geometry(geo);
+  const int64_t e0 = (int64_t)geo->rank * g.chunk;
+  ReduceArgs a;
+  memset(&a, 0, sizeof a);
+  for (int q = 0; q < geo->nranks; ++q) {
+    a.codes[q] = q == geo->rank ? nullptr : recv_codes[q];
+    a.scales[q] = q == geo->rank ? nullptr : recv_scales[q];
+  }
+  a.out_codes = own_codes2;
+  a.out_scales = own_scales2;
+  a.y = y + e0;
+  a.x = x + e0;
+  a.groups = g.chunk_groups;
+  a.rank = geo->rank;
+  return launch_reduce<kOwnPlain>(geo->nranks, a, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -478,6 +514,50 @@ int echo_call(const echo_state* st, const uint16_t* x, const uint8_t* const* rec
   rc = run_reduce_own(st, x, recv_codes, recv_scales, own_codes2, own_scales2, y, s);
   if (rc) return rc;
   return run_exit(st, gath_codes, gath_scales, y, s);
+}
+
+int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
+                    const uint8_t* const* recv_codes, const float* const* recv_scales,
+                    const uint8_t* const* gath_codes, const float* const* gath_scales,
+                    uint8_t* send_codes, float* send_scales, uint8_t* own_codes2,
+                    float* own_scales2, uint16_t* y, echo_stream_t stream) {
+  int rc = check_ranks_shape(n, nranks);
+  if (rc) return rc;
+  if (rank < 0 || rank >= nranks) return ECHO_ERR_RANKS;
+  if (!x || !send_codes || !send_scales || !own_codes2 || !own_scales2 || !y)
+    return ECHO_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(send_codes, 16) || !aligned(send_scales, 4) ||
+      !aligned(own_codes2, 16) || !aligned(own_scales2, 4) || !aligned(y, 16))
+    return ECHO_ERR_ALIGNMENT;
+  // geometry only: the uncompensated call has no averages
+  echo_state geo;
+  geo.m_fast = nullptr;
+  geo.m_slow = nullptr;
+  geo.n = n;
+  geo.nranks = nranks;
+  geo.rank = rank;
+  rc = check_remote_arrays(&geo, recv_codes, recv_scales);
+  if (rc) return rc;
+  rc = check_remote_arrays(&geo, gath_codes, gath_scales);
+  if (rc) return rc;
+  const Geometry g = geometry(&geo);
+  Aliases al;
+  al.out(send_codes, g.n / 2);
+  al.out(send_scales, g.n / ECHO_GROUP * 4);
+  al.out(own_codes2, g.chunk / 2);
+  al.out(own_scales2, g.chunk / ECHO_GROUP * 4);
+  al.out(y, g.n * 2);
+  al.in(x, g.n * 2);
+  add_remote_inputs(al, &geo, recv_codes, recv_scales, g.chunk);
+  add_remote_inputs(al, &geo, gath_codes, gath_scales, g.chunk);
+  al.allow_identical(y, x);
+  if (!al.ok()) return ECHO_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  rc = run_entry_plain(&geo, x, send_codes, send_scales, s);
+  if (rc) return rc;
+  rc = run_reduce_plain(&geo, x, recv_codes, recv_scales, own_codes2, own_scales2, y, s);
+  if (rc) return rc;
+  return run_exit(&geo, gath_codes, gath_scales, y, s);
 }
 
 int echo_get_config(echo_config* out) {

@@ -168,9 +168,14 @@ __device__ __forceinline__ void refresh(float& mf, float& ms, float r) {
 }
 
 // ---------------------------------------------------------------------------
-// stage-1 kernel: entry pass / plain encode / plain update
+// stage-1 kernel: entry pass / plain encode / plain update / uncompensated entry
 
-enum Stage1Mode { kEncode = 0, kEntryFused = 1, kUpdate = 2 };
+enum Stage1Mode { kEncode = 0, kEntryFused = 1, kUpdate = 2, kEntryPlain = 3 };
+
+// what each stage-1 mode does
+constexpr bool skips_own(int m) { return m == kEntryFused || m == kEntryPlain; }
+constexpr bool reads_state(int m) { return m != kEntryPlain; }
+constexpr bool writes_state(int m) { return m == kEntryFused || m == kUpdate; }
 
 struct Stage1Args {
   const uint16_t* x;      // [n]
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
       uint32_t v = 2u * (s0 + u) + half;
       ok[u] = (s0 + u < nslices) && (v < a.groups_work);
       uint32_t gg = v;
-      if (MODE == kEntryFused) gg = v < a.own_g0 ? v : v + own_len;
+      if (skips_own(MODE)) gg = v < a.own_g0 ? v : v + own_len;
       g[u] = ok[u] ? gg : 0u;
       const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
       uint2 xw = make_uint2(0u, 0u);
@@ -218,11 +223,13 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
       own[u] = ok[u] && g[u] >= a.own_g0 && g[u] < a.own_g1;
       if (ok[u]) {
         const u32x2 xv = ld_stream(reinterpret_cast<const u32x2*>(a.x + e));
-        const f32x4 fv = ld_stream(reinterpret_cast<const f32x4*>(a.mf + e));
-        const f32x4 sv = ld_stream(reinterpret_cast<const f32x4*>(a.ms + e));
         xw = make_uint2(xv.x, xv.y);
-        f = make_float4(fv.x, fv.y, fv.z, fv.w);
-        s = make_float4(sv.x, sv.y, sv.z, sv.w);
+        if (reads_state(MODE)) {
+          const f32x4 fv = ld_stream(reinterpret_cast<const f32x4*>(a.mf + e));
+          const f32x4 sv = ld_stream(reinterpret_cast<const f32x4*>(a.ms + e));
+          f = make_float4(fv.x, fv.y, fv.z, fv.w);
+          s = make_float4(sv.x, sv.y, sv.z, sv.w);
+        }
         if (MODE == kUpdate) {
           cw[u] = *reinterpret_cast<const uint16_t*>(a.codes + e / 2);
           sc[u] = a.scales[g[u]];
@@ -241,7 +248,8 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
     for (int u = 0; u < U; ++u) {
       float xp[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) xp[k] = corrected(xf[u][k], mf[u][k], ms[u][k]);
+      for (int k = 0; k < 4; ++k)
+        xp[k] = reads_state(MODE) ? corrected(xf[u][k], mf[u][k], ms[u][k]) : xf[u][k];
 
       float d1[4];
       if (MODE == kUpdate) {
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
         for (int k = 0; k < 4; ++k) d1[k] = (float)q[k] * s;
       }
 
-      if (MODE != kEncode) {
+      if (writes_state(MODE)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           float r = d1[k] - xp[k];
@@ -284,7 +292,10 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
 // ---------------------------------------------------------------------------
 // reduce kernel: rank-order sum of P stage-1 shards of one chunk, requantize
 
-enum ReduceMode { kShard = 0, kOwnFused = 1 };
+enum ReduceMode { kShard = 0, kOwnFused = 1, kOwnPlain = 2 };
+
+// the own slot is quantized in registers from x (with or without the averages)
+constexpr bool own_in_registers(int m) { return m == kOwnFused || m == kOwnPlain; }
 
 struct ReduceArgs {
   const uint8_t* codes[kMaxRanks];   // shard q codes, chunk-local
@@ -293,11 +304,11 @@ struct ReduceArgs {
   float* out_scales;                 // [chunk/128]
   uint16_t* y;                       // [chunk] (nullable in kShard)
   float* e2;                         // [chunk] (kShard, nullable)
-  const uint16_t* x;                 // kOwnFused: own chunk of x
+  const uint16_t* x;                 // kOwnFused / kOwnPlain: own chunk of x
   float* mf;                         // kOwnFused: own chunk of the averages
   float* ms;
   uint32_t groups;                   // groups in the chunk
-  int32_t rank;                      // kOwnFused: the slot computed in registers
+  int32_t rank;                      // kOwnFused / kOwnPlain: the slot computed in registers
 };
 
 template <int MODE, int P, int U>
@@ -326,20 +337,22 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       for (int q = 0; q < P; ++q) {
         cw[u][q] = 0u;
         sc[u][q] = 0.f;
-        if (ok[u] && !(MODE == kOwnFused && q == a.rank)) {
+        if (ok[u] && !(own_in_registers(MODE) && q == a.rank)) {
           cw[u][q] = *reinterpret_cast<const uint16_t*>(a.codes[q] + e / 2);
           sc[u][q] = a.scales[q][g[u]];
         }
       }
       uint2 xw = make_uint2(0u, 0u);
       float4 f = make_float4(0.f, 0.f, 0.f, 0.f), s = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (MODE == kOwnFused && ok[u]) {
+      if (own_in_registers(MODE) && ok[u]) {
         const u32x2 xv = ld_stream(reinterpret_cast<const u32x2*>(a.x + e));
-        const f32x4 fv = ld_stream(reinterpret_cast<const f32x4*>(a.mf + e));
-        const f32x4 sv = ld_stream(reinterpret_cast<const f32x4*>(a.ms + e));
         xw = make_uint2(xv.x, xv.y);
-        f = make_float4(fv.x, fv.y, fv.z, fv.w);
-        s = make_float4(sv.x, sv.y, sv.z, sv.w);
+        if (MODE == kOwnFused) {
+          const f32x4 fv = ld_stream(reinterpret_cast<const f32x4*>(a.mf + e));
+          const f32x4 sv = ld_stream(reinterpret_cast<const f32x4*>(a.ms + e));
+          f = make_float4(fv.x, fv.y, fv.z, fv.w);
+          s = make_float4(sv.x, sv.y, sv.z, sv.w);
+        }
       }
       unpack_bf16x4(xw, xf[u]);
       mf[u][0] = f.x; mf[u][1] = f.y; mf[u][2] = f.z; mf[u][3] = f.w;
@@ -351,9 +364,10 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
       // own stage-1 quantization, in registers (same helpers as the entry pass)
       float xp[4] = {0.f, 0.f, 0.f, 0.f}, d_own[4] = {0.f, 0.f, 0.f, 0.f};
-      if (MODE == kOwnFused) {
+      if (own_in_registers(MODE)) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) xp[k] = corrected(xf[u][k], mf[u][k], ms[u][k]);
+        for (int k = 0; k < 4; ++k)
+          xp[k] = MODE == kOwnFused ? corrected(xf[u][k], mf[u][k], ms[u][k]) : xf[u][k];
         uint32_t m = max(max(abs_bits(xp[0]), abs_bits(xp[1])), max(abs_bits(xp[2]), abs_bits(xp[3])));
         m = halfwave_max(m);
         const float s1 = scale_of(m);
@@ -369,7 +383,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           float d;
-          if (MODE == kOwnFused && q == a.rank) d = d_own[k];
+          if (own_in_registers(MODE) && q == a.rank) d = d_own[k];
           else d = (float)nib(cw[u][q], k) * sc[u][q];
           S[k] = (q == 0) ? d : S[k] + d;
         }

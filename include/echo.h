@@ -189,6 +189,28 @@ int echo_call(const echo_state* st, const uint16_t* x, const uint8_t* const* rec
               const float* const* gath_scales, uint8_t* send_codes, float* send_scales,
               uint8_t* own_codes2, float* own_scales2, uint16_t* y, echo_stream_t stream);
 
+/* The uncompensated 4-bit all-reduce compute path: the same three phases with
+ * x' = f32(x) and no averages (the pages' "uncompensated 4-bit all-reduce",
+ * "Tensor-parallel traffic drops to 4 bits", Interpretation).  Arguments as
+ * echo_call, with the rank geometry given directly.  Also the control of the
+ * deep-chain experiment, and the critical path the compensation is measured
+ * against. */
+int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
+                    const uint8_t* const* recv_codes, const float* const* recv_scales,
+                    const uint8_t* const* gath_codes, const float* const* gath_scales,
+                    uint8_t* send_codes, float* send_scales, uint8_t* own_codes2,
+                    float* own_scales2, uint16_t* y, echo_stream_t stream);
+
+/* Deferred update.  The pages run the averages' update beside the next matrix
+ * multiplication, off the critical path ("Tensor-parallel traffic drops to 4
+ * bits", Interpretation).  With this API that schedule is: echo_encode (the
+ * whole tensor, averages read-only; chunk p of its output is the own stage-1
+ * message) -> transport -> echo_reduce_shard (slot p = that own message, out_e2
+ * kept) -> transport -> echo_call_exit on the critical stream; then echo_update
+ * (codes1 = the echo_encode output, e2_own) on a side stream, which must finish
+ * before the next call's entry pass reads the averages.  Bit-identical to
+ * echo_call. */
+
 /* ---- misc ------------------------------------------------------------------ */
 int echo_get_config(echo_config* out);      /* the named parameters above */
 const char* echo_status_string(int status); /* static string, never NULL */

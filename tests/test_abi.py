@@ -25,7 +25,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("echo_state_init", "echo_encode", "echo_reduce_shard", "echo_decode",
                  "echo_update", "echo_call", "echo_call_entry", "echo_call_reduce",
-                 "echo_call_exit", "echo_get_config", "echo_status_string", "echo_version"):
+                 "echo_call_exit", "echo_call_plain", "echo_get_config", "echo_status_string",
+                 "echo_version"):
         assert want in names
 
 
@@ -145,3 +146,21 @@ def test_call_rejections():
     assert rc(B.echo_call_reduce, s4, 3 * A, recv_c, recv_s, 52 * A, 53 * A, None) == -1
     assert rc(B.echo_call_exit, s4, gath_c, gath_s, A) == -6  # y over m_fast
     assert rc(B.echo_call_entry, st(n=n, P=P, rank=4), 3 * A, 50 * A, 51 * A) == -4
+
+
+def test_call_plain_rejections():
+    P, n = 4, 4096
+    recv_c = [10 * A + k * A for k in range(P)]
+    recv_s = [20 * A + k * A for k in range(P)]
+    gath_c = [30 * A + k * A for k in range(P)]
+    gath_s = [40 * A + k * A for k in range(P)]
+    outs = [50 * A, 51 * A, 52 * A, 53 * A, 54 * A]
+    assert rc(B.echo_call_plain, P, 4, 3 * A, recv_c, recv_s, gath_c, gath_s, *outs, n) == -4
+    assert rc(B.echo_call_plain, 0, 0, 3 * A, recv_c, recv_s, gath_c, gath_s, *outs, n) == -4
+    assert rc(B.echo_call_plain, P, 1, 3 * A, recv_c, recv_s, gath_c, gath_s, *outs, 1000) == -2
+    assert rc(B.echo_call_plain, P, 1, 3 * A + 8, recv_c, recv_s, gath_c, gath_s, *outs, n) == -3
+    bad = list(recv_c)
+    bad[3] = None
+    assert rc(B.echo_call_plain, P, 1, 3 * A, bad, recv_s, gath_c, gath_s, *outs, n) == -1
+    assert rc(B.echo_call_plain, P, 1, 3 * A, recv_c, recv_s, gath_c, gath_s, 50 * A, 51 * A,
+              52 * A, 53 * A, 3 * A + 32, n) == -6

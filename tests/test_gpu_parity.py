@@ -332,3 +332,71 @@ def test_full_simulation_small(P, k, calls):
             eq(g.host(r.y, np.uint16), want["y"], f"y rank {p}")
             eq(g.host(r.mf, np.float32), mf[p], f"m_fast rank {p}")
             eq(g.host(r.ms, np.float32), ms[p], f"m_slow rank {p}")
+
+
+@pytest.mark.parametrize("P,rank,k", [(1, 0, 3), (2, 1, 5), (3, 2, 4), (8, 0, 9), (8, 6, 33), (16, 9, 2)])
+def test_call_plain_uncompensated(P, rank, k):
+    """The uncompensated call against the oracle with compensation off."""
+    g = gu()
+    case = RankCase(P, rank, k, seed=300 + P + k)
+    n = case.n
+    for call in range(2):
+        x = x_of(n, 700 + call + k)
+        B.echo_call_plain(P, rank, g.dev(x), case.slot(case.recv_d, 0), case.slot(case.recv_d, 1),
+                          case.slot(case.gath_d, 0), case.slot(case.gath_d, 1), case.send_c,
+                          case.send_s, case.own_c, case.own_s, case.y)
+        want = orc.call(P, rank, x, None, None, case.slot(case.recv, 0), case.slot(case.recv, 1),
+                        case.slot(case.gath, 0), case.slot(case.gath, 1), comp=False)
+        case.check(want)  # the averages stay untouched (zero), as the oracle's
+
+
+@pytest.mark.parametrize("P,rank,k", [(8, 3, 9), (4, 0, 5)])
+def test_deferred_update_on_side_stream_equals_fused(P, rank, k):
+    """The critical-path split: encode + reduce_shard + exit on the main
+    stream, the averages' update on a side stream (beside a matmul that
+    consumes y), ordered by events; bit-identical to the fused call."""
+    g = gu()
+    fused = RankCase(P, rank, k, seed=61)
+    split = RankCase(P, rank, k, seed=61)
+    n, Cn = fused.n, fused.Cn
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    codes1, scales1 = g.empty_u8(n // 2), g.empty_f32(n // 128)
+    e2 = g.empty_f32(Cn)
+    updated = None
+    w = torch.randn(128, 64, device=g.DEV, dtype=torch.bfloat16)
+    for call in range(4):
+        x = x_of(n, 40 + call)
+        xd = g.dev(x)
+        fused.gpu_call(xd)
+        if updated is not None:
+            main.wait_event(updated)  # the next entry pass reads the averages
+        B.echo_encode(split.st, xd, codes1, scales1, stream=main)
+        sh_c = [codes1[rank * Cn // 2:(rank + 1) * Cn // 2] if q == rank else split.recv_d[q][0]
+                for q in range(P)]
+        sh_s = [scales1[rank * Cn // 128:(rank + 1) * Cn // 128] if q == rank else split.recv_d[q][1]
+                for q in range(P)]
+        B.echo_reduce_shard(sh_c, sh_s, split.own_c, split.own_s, split.y[rank * Cn:(rank + 1) * Cn],
+                            e2, chunk_n=Cn, stream=main)
+        reduced = torch.cuda.Event()
+        reduced.record(main)
+        B.echo_call_exit(split.st, split.slot(split.gath_d, 0), split.slot(split.gath_d, 1), split.y,
+                         stream=main)
+        # the next layer's matmul on the critical stream consumes y
+        h = split.y.view(torch.bfloat16).reshape(-1, 128) @ w
+        side.wait_event(reduced)
+        B.echo_update(split.st, xd, codes1, scales1, e2, stream=side)
+        updated = torch.cuda.Event()
+        updated.record(side)
+        xd.record_stream(side)
+        torch.cuda.synchronize()
+        assert torch.isfinite(h.float()).all()
+        g.eq(g.host(split.y, np.uint16), g.host(fused.y, np.uint16), f"call {call} y")
+        g.eq(g.host(split.own_c, np.uint8), g.host(fused.own_c, np.uint8), f"call {call} codes2")
+        g.eq(g.host(split.mfd, np.float32), g.host(fused.mfd, np.float32), f"call {call} m_fast")
+        g.eq(g.host(split.msd, np.float32), g.host(fused.msd, np.float32), f"call {call} m_slow")
+        c1 = g.host(codes1, np.uint8)
+        fc = g.host(fused.send_c, np.uint8)
+        for j in range(P):
+            if j != rank:
+                g.eq(c1[j * Cn // 2:(j + 1) * Cn // 2], fc[j * Cn // 2:(j + 1) * Cn // 2], "send")
