@@ -155,16 +155,18 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
 
     state = {"updated": None}
 
-    def split_critical():
+    def wait_update():
         if state["updated"] is not None:
             main.wait_event(state["updated"])
+
+    def split_critical():
         B.echo_encode(st, xd, send_c, send_s, main)
         B.echo_reduce_shard(sh_c, sh_s, own_c, own_s, y[rank * C:(rank + 1) * C], e2, chunk_n=C,
                             stream=main)
-        reduced = torch.cuda.Event()
-        reduced.record(main)
         B.echo_call_exit(st, gc_, gs_, y, main)
-        return reduced
+        done = torch.cuda.Event()  # the update starts once the critical path is done
+        done.record(main)
+        return done
 
     def split_update(reduced):
         side.wait_event(reduced)
@@ -204,6 +206,7 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         gemm()
 
     def b_split(e=None):
+        wait_update()  # the entry pass reads the averages the previous update wrote
         if e: e[0].record(main)
         reduced = split_critical()
         if e: e[1].record(main)

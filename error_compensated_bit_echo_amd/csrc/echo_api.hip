@@ -35,6 +35,12 @@ namespace {
 #ifndef ECHO_U_EXIT
 #define ECHO_U_EXIT 2
 #endif
+#ifndef ECHO_U_PLAIN
+#define ECHO_U_PLAIN 2
+#endif
+#ifndef ECHO_U_REDUCE_PLAIN
+#define ECHO_U_REDUCE_PLAIN 1
+#endif
 constexpr uint32_t kMaxBlocks = ECHO_MAX_BLOCKS;
 constexpr int kU1 = ECHO_U_STAGE1;  // stage-1 slices (2 groups each) per wave step
 constexpr int kUR = ECHO_U_REDUCE;  // reduce slices per wave step
@@ -106,25 +112,38 @@ class Aliases {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? ECHO_SUCCESS : ECHO_ERR_HIP; }
 
+#ifndef ECHO_UPDATE_MAX_BLOCKS
+#define ECHO_UPDATE_MAX_BLOCKS ECHO_MAX_BLOCKS
+#endif
+
+// slices per wave step for each stage-1 mode: the uncompensated entry pass
+// moves only 2.5 bytes per element, so its waves take more work each
+constexpr int u_stage1(int mode) { return mode == kEntryPlain ? ECHO_U_PLAIN : kU1; }
+
 template <int MODE>
 int launch_stage1(const Stage1Args& a, hipStream_t s) {
+  constexpr int U = u_stage1(MODE);
   const uint64_t nslices = ((uint64_t)a.groups_work + 1) / 2;
   if (nslices == 0) return ECHO_SUCCESS;
-  const uint32_t blocks = blocks_for((nslices + kU1 - 1) / kU1);
-  hipLaunchKernelGGL((k_stage1<MODE, kU1>), dim3(blocks), dim3(kBlock), 0, s, a);
+  uint32_t blocks = blocks_for((nslices + U - 1) / U);
+  if (MODE == kUpdate && blocks > (uint32_t)ECHO_UPDATE_MAX_BLOCKS) blocks = ECHO_UPDATE_MAX_BLOCKS;
+  hipLaunchKernelGGL((k_stage1<MODE, U>), dim3(blocks), dim3(kBlock), 0, s, a);
   return launch_status();
 }
 
+constexpr int u_reduce(int mode) { return mode == kOwnFused ? kUR : ECHO_U_REDUCE_PLAIN; }
+
 template <int MODE, int P>
 void launch_reduce_p(const ReduceArgs& a, uint32_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL((k_reduce<MODE, P, kUR>), dim3(blocks), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL((k_reduce<MODE, P, u_reduce(MODE)>), dim3(blocks), dim3(kBlock), 0, s, a);
 }
 
 template <int MODE>
 int launch_reduce(int P, const ReduceArgs& a, hipStream_t s) {
+  constexpr int U = u_reduce(MODE);
   const uint64_t nslices = ((uint64_t)a.groups + 1) / 2;
   if (nslices == 0) return ECHO_SUCCESS;
-  const uint32_t blocks = blocks_for((nslices + kUR - 1) / kUR);
+  const uint32_t blocks = blocks_for((nslices + U - 1) / U);
   switch (P) {
 #define ECHO_REDUCE_CASE(p) \
   case p: launch_reduce_p<MODE, p>(a, blocks, s); break;

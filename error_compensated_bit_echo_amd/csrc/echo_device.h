@@ -143,7 +143,10 @@ __device__ __forceinline__ float scale_of(uint32_t amax_bits) {
 // |v| / 1 < 0.5 rounds to code 0 -- the same codes as the zero-group rule.
 __device__ __forceinline__ float code_divisor(float s) { return s == 0.0f ? 1.0f : s; }
 
-// code = clamp(rint(v / s), -7, 7)
+// code = clamp(rint(v / s), -7, 7), v / s the correctly rounded division.
+// (A reciprocal-multiply with an exact fallback near half-integers gives the
+// same codes but measured no faster on MI355X: these kernels are not bound
+// by the division.)
 __device__ __forceinline__ int quant_code(float v, float sdiv) {
   float t = __builtin_rintf(v / sdiv);
   t = fminf(fmaxf(t, -kQmax), kQmax);

@@ -400,3 +400,96 @@ def test_deferred_update_on_side_stream_equals_fused(P, rank, k):
         for j in range(P):
             if j != rank:
                 g.eq(c1[j * Cn // 2:(j + 1) * Cn // 2], fc[j * Cn // 2:(j + 1) * Cn // 2], "send")
+
+
+def _adversarial_groups(rng, ngroups):
+    """x' values placed on the quantizer's decision boundaries.  Each group:
+    element 0 is the absmax A, s = fl(A / 7), and the rest are fl((k + 1/2) s)
+    for k in -7..6 together with their 1-3 ulp neighbours, in random order;
+    scales range over normal, denormal and near-overflow magnitudes."""
+    vals = np.zeros((ngroups, 128), np.float32)
+    for gi in range(ngroups):
+        kind = gi % 6
+        if kind == 0:
+            A = np.float32(rng.uniform(0.5, 8.0))
+        elif kind == 1:
+            A = np.float32(7.0 * 2.0 ** rng.integers(-20, 20))  # s a power of two: exact ties
+        elif kind == 2:
+            A = np.float32(rng.uniform(1.0, 1000.0) * 2.0 ** -135)  # denormal scale
+        elif kind == 3:
+            A = np.float32(rng.uniform(1.0, 6.0) * 2.0 ** 124)  # scale near 2^126
+        elif kind == 4:
+            A = np.float32(rng.uniform(1e-30, 1e-20))
+        else:
+            A = np.float32(rng.uniform(1e20, 1e30))
+        s = np.float32(A / np.float32(7.0))
+        cand = []
+        for k in range(-7, 7):
+            t = np.float32(np.float32(k + 0.5) * s)
+            cand.append(t)
+            up, dn = t, t
+            for _ in range(3):
+                up = np.nextafter(up, np.float32(np.inf))
+                dn = np.nextafter(dn, np.float32(-np.inf))
+                cand += [up, dn]
+        cand = np.array(cand, np.float32)
+        cand = cand[np.abs(cand) <= A]
+        rng.shuffle(cand)
+        row = np.zeros(128, np.float32)
+        row[0] = A if rng.random() < 0.5 else -A
+        m = min(127, cand.size)
+        row[1:1 + m] = cand[:m]
+        vals[gi] = row
+    return vals.ravel()
+
+
+def test_quantizer_decision_boundaries():
+    """Codes for quotients exactly on, and a few ulps beside, every rounding
+    boundary -- the cases where a reciprocal-multiply could disagree with the
+    correctly rounded division -- match the oracle bit for bit."""
+    g = gu()
+    rng = np.random.default_rng(123)
+    t = _adversarial_groups(rng, 6 * 200)
+    n = t.size
+    x = np.zeros(n, np.uint16)                 # x' = 0 - (0.5 * (-2t) + 0.5 * 0) = t exactly
+    mf = (np.float32(-2.0) * t).astype(np.float32)
+    ms = np.zeros(n, np.float32)
+    assert np.all(np.isfinite(mf))
+    st = B.EchoState(g.dev(mf), g.dev(ms), n, 1, 0)
+    codes, scales = g.empty_u8(n // 2), g.empty_f32(n // 128)
+    B.echo_encode(st, g.dev(x), codes, scales)
+    want_c, want_s, xp = orc.encode(x, mf, ms, want_xp=True)
+    assert np.array_equal(xp.view(np.uint32), t.view(np.uint32))  # the construction holds
+    eq(g.host(scales, np.float32), want_s, "scales")
+    eq(g.host(codes, np.uint8), want_c, "codes")
+
+
+@pytest.mark.parametrize("ulps", [0, 1, -1, 3])
+def test_requantizer_decision_boundaries(ulps):
+    """The reduce stage's quantizer on sums that sit on half-integers of the
+    stage-2 scale: shard 0 carries codes with scale s0 (one code 7 per group
+    fixes amax = 7 s0), shard 1 odd codes with scale s0/2 moved by `ulps`, so
+    S / s2 = c0 + c1/2 (+ a few ulps)."""
+    g = gu()
+    rng = np.random.default_rng(77 + ulps)
+    groups = 512
+    cn = 128 * groups
+    q0 = rng.integers(-4, 5, cn).astype(np.int8)  # |c0 + c1/2| <= 6.5 < 7: amax stays 7 s0
+    q0[::128] = 7
+    q1 = (rng.integers(-3, 3, cn) * 2 + 1).astype(np.int8)
+    q1[::128] = 0
+    s0 = rng.uniform(0.01, 100.0, groups).astype(np.float32)
+    s0[::2] = (2.0 ** rng.integers(-30, 30, groups // 2)).astype(np.float32)  # s2 == s0: exact ties
+    s1 = (s0 / np.float32(2.0)).astype(np.float32)
+    for _ in range(abs(ulps)):
+        s1 = np.nextafter(s1, np.float32(np.inf if ulps > 0 else -np.inf)).astype(np.float32)
+    msgs = [(orc.pack(q0), s0), (orc.pack(q1), s1)]
+    out_c, out_s = g.empty_u8(cn // 2), g.empty_f32(cn // 128)
+    out_y, out_e2 = g.empty_bf16(cn), g.empty_f32(cn)
+    B.echo_reduce_shard([g.dev(c) for c, _ in msgs], [g.dev(sc) for _, sc in msgs], out_c, out_s,
+                        out_y, out_e2, chunk_n=cn)
+    wc, ws, wy, we = orc.reduce_chunk([c for c, _ in msgs], [sc for _, sc in msgs], cn)
+    eq(g.host(out_s, np.float32), ws, "scales2")
+    eq(g.host(out_c, np.uint8), wc, "codes2")
+    eq(g.host(out_y, np.uint16), wy, "y")
+    eq(g.host(out_e2, np.float32), we, "e2")
