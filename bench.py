@@ -40,6 +40,14 @@ def bytes_per_element(P: int) -> dict:
     }
 
 
+def rs_bytes(N: int, P: int) -> float:
+    """Algorithmic bytes of the reduce-scatter call: the entry pass plus the
+    own chunk's x, averages, P-1 incoming shards and bf16 output."""
+    code = 0.5 + 4.0 / 128.0
+    C = N // P
+    return (N - C) * bytes_per_element(P)["entry"] + C * (2 + 16 + code * (P - 1) + 2)
+
+
 def step_bytes(N: int, P: int) -> float:
     b = bytes_per_element(P)
     C = N // P
@@ -223,9 +231,16 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         B.echo_update(st, xd, send_c, send_s, e2, main)
         if e: e[1].record(main)
 
+    y_own = torch.empty(C, dtype=torch.int16, device=y.device)
+
+    def b_rs(e=None):
+        if e: e[0].record(main)
+        B.echo_rs_call(st, xd, rc_, rs_, send_c, send_s, y_own, main)
+        if e: e[1].record(main)
+
     out = {}
     for name, body in (("gemm", b_gemm), ("fused", b_fused), ("plain", b_plain), ("split", b_split),
-                       ("update_alone", b_update)):
+                       ("update_alone", b_update), ("rs", b_rs)):
         wall, first = timed(body)
         out[name] = (wall, first)
     torch.cuda.synchronize()
@@ -238,6 +253,8 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         "update_alone_ms": round(out["update_alone"][1], 4),
         "layer_ms": {"fused+matmul": round(out["fused"][0], 4), "plain+matmul": round(out["plain"][0], 4),
                      "split+matmul(update beside it)": round(out["split"][0], 4)},
+        "reduce_scatter_call_ms": round(out["rs"][1], 4),
+        "reduce_scatter_GBps": round(rs_bytes(N, P) / (out["rs"][1] * 1e-3) / 1e9, 1),
         "compensation_on_critical_path_ms": {
             "fused": round(out["fused"][1] - out["plain"][1], 4),
             "split": round(out["split"][1] - out["plain"][1], 4)},

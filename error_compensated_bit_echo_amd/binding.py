@@ -54,6 +54,9 @@ _SIGNATURES = {
     "echo_call": [C.POINTER(EchoStateC), _vp, _pp, _pp, _pp, _pp, _vp, _vp, _vp, _vp, _vp, _vp],
     "echo_call_plain": [C.c_int32, C.c_int32, C.c_int64, _vp, _pp, _pp, _pp, _pp, _vp, _vp, _vp,
                         _vp, _vp, _vp],
+    "echo_reduce_shard_sum": [C.c_int32, C.c_int64, _pp, _pp, _vp, _vp, _vp],
+    "echo_rs_reduce": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp],
+    "echo_rs_call": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp, _vp, _vp],
     "echo_get_config": [C.POINTER(EchoConfigC)],
     "echo_status_string": [C.c_int],
     "echo_version": [],
@@ -197,6 +200,27 @@ def echo_call_plain(nranks, rank, x, recv_codes, recv_scales, gath_codes, gath_s
                                _ptrs(recv_scales), _ptrs(gath_codes), _ptrs(gath_scales),
                                _ptr(send_codes), _ptr(send_scales), _ptr(own_codes2),
                                _ptr(own_scales2), _ptr(y), _stream(stream)), "echo_call_plain")
+
+
+def echo_reduce_shard_sum(shard_codes, shard_scales, out_y, out_e2=None, chunk_n=None,
+                          stream=None) -> None:
+    if chunk_n is None:
+        chunk_n = out_y.numel()
+    _check(lib.echo_reduce_shard_sum(len(shard_codes), int(chunk_n), _ptrs(shard_codes),
+                                     _ptrs(shard_scales), _ptr(out_y), _ptr(out_e2),
+                                     _stream(stream)), "echo_reduce_shard_sum")
+
+
+def echo_rs_reduce(st: EchoState, x, recv_codes, recv_scales, y_own, stream=None) -> None:
+    _check(lib.echo_rs_reduce(C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
+                              _ptr(y_own), _stream(stream)), "echo_rs_reduce")
+
+
+def echo_rs_call(st: EchoState, x, recv_codes, recv_scales, send_codes, send_scales, y_own,
+                 stream=None) -> None:
+    _check(lib.echo_rs_call(C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
+                            _ptr(send_codes), _ptr(send_scales), _ptr(y_own), _stream(stream)),
+           "echo_rs_call")
 
 
 def echo_get_config() -> dict:

@@ -131,7 +131,9 @@ int launch_stage1(const Stage1Args& a, hipStream_t s) {
   return launch_status();
 }
 
-constexpr int u_reduce(int mode) { return mode == kOwnFused ? kUR : ECHO_U_REDUCE_PLAIN; }
+constexpr int u_reduce(int mode) {
+  return (mode == kOwnFused || mode == kOwnRS) ? kUR : ECHO_U_REDUCE_PLAIN;
+}
 
 template <int MODE, int P>
 void launch_reduce_p(const ReduceArgs& a, uint32_t blocks, hipStream_t s) {
@@ -295,6 +297,40 @@ int run_reduce_plain(const echo_state* geo, const uint16_t* x, const uint8_t* co
   a.groups = g.chunk_groups;
   a.rank = geo->rank;
   return launch_reduce<kOwnPlain>(geo->nranks, a, s);
+}
+
+// ---- reduce-scatter only -----------------------------------------------------
+
+int run_rs_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
+                  const float* const* recv_scales, uint16_t* y_own, hipStream_t s) {
+  const Geometry g = geometry(st);
+  const int64_t e0 = (int64_t)st->rank * g.chunk;
+  ReduceArgs a;
+  memset(&a, 0, sizeof a);
+  for (int q = 0; q < st->nranks; ++q) {
+    a.codes[q] = q == st->rank ? nullptr : recv_codes[q];
+    a.scales[q] = q == st->rank ? nullptr : recv_scales[q];
+  }
+  a.y = y_own;
+  a.x = x + e0;
+  a.mf = st->m_fast + e0;
+  a.ms = st->m_slow + e0;
+  a.groups = g.chunk_groups;
+  a.rank = st->rank;
+  return launch_reduce<kOwnRS>(st->nranks, a, s);
+}
+
+int check_rs_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
+                    const float* const* recv_scales, uint16_t* y_own, Aliases& al) {
+  if (!x || !y_own) return ECHO_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(y_own, 16)) return ECHO_ERR_ALIGNMENT;
+  int rc = check_remote_arrays(st, recv_codes, recv_scales);
+  if (rc) return rc;
+  const Geometry g = geometry(st);
+  al.out(y_own, g.chunk * 2);
+  al.in(x, g.n * 2);
+  add_remote_inputs(al, st, recv_codes, recv_scales, g.chunk);
+  return ECHO_SUCCESS;
 }
 
 }  // namespace
@@ -577,6 +613,73 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
   rc = run_reduce_plain(&geo, x, recv_codes, recv_scales, own_codes2, own_scales2, y, s);
   if (rc) return rc;
   return run_exit(&geo, gath_codes, gath_scales, y, s);
+}
+
+int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
+                          const float* const* shard_scales, uint16_t* out_y, float* out_e2,
+                          echo_stream_t stream) {
+  if (nranks < 1 || nranks > ECHO_MAX_RANKS) return ECHO_ERR_RANKS;
+  if (chunk_n <= 0 || chunk_n > ECHO_MAX_ELEMENTS || chunk_n % ECHO_GROUP != 0) return ECHO_ERR_SHAPE;
+  if (!shard_codes || !shard_scales || !out_y) return ECHO_ERR_INVALID_ARGUMENT;
+  for (int q = 0; q < nranks; ++q) {
+    if (!shard_codes[q] || !shard_scales[q]) return ECHO_ERR_INVALID_ARGUMENT;
+    if (!aligned(shard_codes[q], 16) || !aligned(shard_scales[q], 4)) return ECHO_ERR_ALIGNMENT;
+  }
+  if (!aligned(out_y, 16) || !aligned(out_e2, 16)) return ECHO_ERR_ALIGNMENT;
+  Aliases al;
+  al.out(out_y, chunk_n * 2);
+  al.out(out_e2, chunk_n * 4);
+  for (int q = 0; q < nranks; ++q) {
+    al.in(shard_codes[q], chunk_n / 2);
+    al.in(shard_scales[q], chunk_n / ECHO_GROUP * 4);
+  }
+  if (!al.ok()) return ECHO_ERR_ALIAS;
+  ReduceArgs a;
+  memset(&a, 0, sizeof a);
+  for (int q = 0; q < nranks; ++q) {
+    a.codes[q] = shard_codes[q];
+    a.scales[q] = shard_scales[q];
+  }
+  a.y = out_y;
+  a.e2 = out_e2;
+  a.groups = (uint32_t)(chunk_n / ECHO_GROUP);
+  a.rank = -1;
+  return launch_reduce<kShardSum>(nranks, a, (hipStream_t)stream);
+}
+
+int echo_rs_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
+                   const float* const* recv_scales, uint16_t* y_own, echo_stream_t stream) {
+  int rc = check_state(st);
+  if (rc) return rc;
+  Aliases al;
+  rc = check_rs_reduce(st, x, recv_codes, recv_scales, y_own, al);
+  if (rc) return rc;
+  al.out(st->m_fast, st->n * 4);
+  al.out(st->m_slow, st->n * 4);
+  if (!al.ok()) return ECHO_ERR_ALIAS;
+  return run_rs_reduce(st, x, recv_codes, recv_scales, y_own, (hipStream_t)stream);
+}
+
+int echo_rs_call(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
+                 const float* const* recv_scales, uint8_t* send_codes, float* send_scales,
+                 uint16_t* y_own, echo_stream_t stream) {
+  int rc = check_state(st);
+  if (rc) return rc;
+  if (!send_codes || !send_scales) return ECHO_ERR_INVALID_ARGUMENT;
+  if (!aligned(send_codes, 16) || !aligned(send_scales, 4)) return ECHO_ERR_ALIGNMENT;
+  Aliases al;
+  rc = check_rs_reduce(st, x, recv_codes, recv_scales, y_own, al);
+  if (rc) return rc;
+  const int64_t n = st->n;
+  al.out(send_codes, n / 2);
+  al.out(send_scales, n / ECHO_GROUP * 4);
+  al.out(st->m_fast, n * 4);
+  al.out(st->m_slow, n * 4);
+  if (!al.ok()) return ECHO_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  rc = run_entry(st, x, send_codes, send_scales, s);
+  if (rc) return rc;
+  return run_rs_reduce(st, x, recv_codes, recv_scales, y_own, s);
 }
 
 int echo_get_config(echo_config* out) {

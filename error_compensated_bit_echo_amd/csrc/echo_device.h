@@ -295,23 +295,28 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
 // ---------------------------------------------------------------------------
 // reduce kernel: rank-order sum of P stage-1 shards of one chunk, requantize
 
-enum ReduceMode { kShard = 0, kOwnFused = 1, kOwnPlain = 2 };
+// kShard / kOwnFused / kOwnPlain: all-reduce (the sum is requantized);
+// kShardSum / kOwnRS: reduce-scatter only (the sum is the bf16 output).
+enum ReduceMode { kShard = 0, kOwnFused = 1, kOwnPlain = 2, kShardSum = 3, kOwnRS = 4 };
 
 // the own slot is quantized in registers from x (with or without the averages)
-constexpr bool own_in_registers(int m) { return m == kOwnFused || m == kOwnPlain; }
+constexpr bool own_in_registers(int m) { return m == kOwnFused || m == kOwnPlain || m == kOwnRS; }
+constexpr bool own_reads_state(int m) { return m == kOwnFused || m == kOwnRS; }
+constexpr bool requantizes(int m) { return m == kShard || m == kOwnFused || m == kOwnPlain; }
+constexpr bool stores_e2(int m) { return m == kShard || m == kShardSum; }
 
 struct ReduceArgs {
   const uint8_t* codes[kMaxRanks];   // shard q codes, chunk-local
   const float* scales[kMaxRanks];    // shard q scales, chunk-local
-  uint8_t* out_codes;                // [chunk/2]
-  float* out_scales;                 // [chunk/128]
-  uint16_t* y;                       // [chunk] (nullable in kShard)
-  float* e2;                         // [chunk] (kShard, nullable)
-  const uint16_t* x;                 // kOwnFused / kOwnPlain: own chunk of x
-  float* mf;                         // kOwnFused: own chunk of the averages
+  uint8_t* out_codes;                // [chunk/2] (requantizing modes)
+  float* out_scales;                 // [chunk/128] (requantizing modes)
+  uint16_t* y;                       // [chunk] (nullable in kShard / kShardSum)
+  float* e2;                         // [chunk] (kShard / kShardSum, nullable)
+  const uint16_t* x;                 // own modes: own chunk of x
+  float* mf;                         // kOwnFused / kOwnRS: own chunk of the averages
   float* ms;
   uint32_t groups;                   // groups in the chunk
-  int32_t rank;                      // kOwnFused / kOwnPlain: the slot computed in registers
+  int32_t rank;                      // own modes: the slot computed in registers
 };
 
 template <int MODE, int P, int U>
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       if (own_in_registers(MODE) && ok[u]) {
         const u32x2 xv = ld_stream(reinterpret_cast<const u32x2*>(a.x + e));
         xw = make_uint2(xv.x, xv.y);
-        if (MODE == kOwnFused) {
+        if (own_reads_state(MODE)) {
           const f32x4 fv = ld_stream(reinterpret_cast<const f32x4*>(a.mf + e));
           const f32x4 sv = ld_stream(reinterpret_cast<const f32x4*>(a.ms + e));
           f = make_float4(fv.x, fv.y, fv.z, fv.w);
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       if (own_in_registers(MODE)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          xp[k] = MODE == kOwnFused ? corrected(xf[u][k], mf[u][k], ms[u][k]) : xf[u][k];
+          xp[k] = own_reads_state(MODE) ? corrected(xf[u][k], mf[u][k], ms[u][k]) : xf[u][k];
         uint32_t m = max(max(abs_bits(xp[0]), abs_bits(xp[1])), max(abs_bits(xp[2]), abs_bits(xp[3])));
         m = halfwave_max(m);
         const float s1 = scale_of(m);
@@ -392,16 +397,24 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
         }
       }
 
-      // stage-2 quantization
-      uint32_t m2 = max(max(abs_bits(S[0]), abs_bits(S[1])), max(abs_bits(S[2]), abs_bits(S[3])));
-      m2 = halfwave_max(m2);
-      const float s2 = scale_of(m2);
-      const float sd2 = code_divisor(s2);
-      int q2[4];
+      // all-reduce: requantize the sum (stage 2), y = bf16(code2 * s2);
+      // reduce-scatter: the sum itself is the output, y = bf16(S)
+      int q2[4] = {0, 0, 0, 0};
+      float s2 = 0.f;
+      uint32_t y01, y23;
+      if (requantizes(MODE)) {
+        uint32_t m2 = max(max(abs_bits(S[0]), abs_bits(S[1])), max(abs_bits(S[2]), abs_bits(S[3])));
+        m2 = halfwave_max(m2);
+        s2 = scale_of(m2);
+        const float sd2 = code_divisor(s2);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) q2[k] = quant_code(S[k], sd2);
-      const uint32_t y01 = pack_bf16x2((float)q2[0] * s2, (float)q2[1] * s2);
-      const uint32_t y23 = pack_bf16x2((float)q2[2] * s2, (float)q2[3] * s2);
+        for (int k = 0; k < 4; ++k) q2[k] = quant_code(S[k], sd2);
+        y01 = pack_bf16x2((float)q2[0] * s2, (float)q2[1] * s2);
+        y23 = pack_bf16x2((float)q2[2] * s2, (float)q2[3] * s2);
+      } else {
+        y01 = pack_bf16x2(S[0], S[1]);
+        y23 = pack_bf16x2(S[2], S[3]);
+      }
       float e2[4];
       e2[0] = bf16_lo(y01) - S[0];
       e2[1] = bf16_hi(y01) - S[1];
@@ -409,13 +422,15 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       e2[3] = bf16_hi(y23) - S[3];
 
       if (ok[u]) {
-        *reinterpret_cast<uint16_t*>(a.out_codes + e / 2) = (uint16_t)pack_nib4(q2);
-        if (sub == 0) a.out_scales[g[u]] = s2;
+        if (requantizes(MODE)) {
+          st_stream(reinterpret_cast<uint16_t*>(a.out_codes + e / 2), (uint16_t)pack_nib4(q2));
+          if (sub == 0) a.out_scales[g[u]] = s2;
+        }
         if (a.y) st_stream(reinterpret_cast<u32x2*>(a.y + e), u32x2{y01, y23});
-        if (MODE == kShard && a.e2)
+        if (stores_e2(MODE) && a.e2)
           *reinterpret_cast<float4*>(a.e2 + e) = make_float4(e2[0], e2[1], e2[2], e2[3]);
       }
-      if (MODE == kOwnFused) {
+      if (own_reads_state(MODE)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float e1 = d_own[k] - xp[k];

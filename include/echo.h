@@ -211,6 +211,34 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
  * before the next call's entry pass reads the averages.  Bit-identical to
  * echo_call. */
 
+/* ---- reduce-scatter only (sequence parallelism) ------------------------------
+ * The pages name the reduce-scatter of sequence parallelism as a natural next
+ * target ("Tensor-parallel traffic drops to 4 bits", Perspective).  Reading:
+ * the entry pass is the all-reduce's; rank p sums the P stage-1 shards of its
+ * chunk in binary32, rank order, and outputs the sum as bf16 (round to nearest
+ * even) -- there is no second quantization, each value is quantized once; the
+ * residual on the own chunk is e = f32(y) - S in place of e2. */
+
+/* Rank-order sum of P stage-1 shards output as bf16: out_y[chunk_n] =
+ * bf16(S); out_e2 (nullable) = f32(out_y) - S.  Unfused. */
+int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
+                          const float* const* shard_scales, uint16_t* out_y, float* out_e2,
+                          echo_stream_t stream);
+
+/* Reduce phase of the reduce-scatter: the own chunk's correction and stage-1
+ * quantization in registers, the rank-order sum with the P-1 incoming shards
+ * (as echo_call_reduce), y_own[n/P] = bf16(S), and the averages' update on
+ * the own chunk with r = e1 + (f32(y_own) - S).  y_own may not overlap x. */
+int echo_rs_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
+                   const float* const* recv_scales, uint16_t* y_own, echo_stream_t stream);
+
+/* The fused reduce-scatter: echo_call_entry then echo_rs_reduce on one stream.
+ * Bit-identical to echo_encode + echo_reduce_shard_sum (own slot = own
+ * stage-1 chunk, out_e2 kept) + echo_update. */
+int echo_rs_call(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
+                 const float* const* recv_scales, uint8_t* send_codes, float* send_scales,
+                 uint16_t* y_own, echo_stream_t stream);
+
 /* ---- misc ------------------------------------------------------------------ */
 int echo_get_config(echo_config* out);      /* the named parameters above */
 const char* echo_status_string(int status); /* static string, never NULL */

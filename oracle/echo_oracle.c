@@ -300,3 +300,87 @@ int orc_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const*
   free(e2);
   return ok ? 0 : -1;
 }
+
+/* ---- reduce-scatter only ------------------------------------------------------ */
+
+void orc_reduce_chunk_sum(int nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
+                          const float* const* shard_scales, uint16_t* y, float* e) {
+  for (int64_t i = 0; i < chunk_n; ++i) {
+    float acc = dequant(shard_codes[0], shard_scales[0], i);
+    for (int r = 1; r < nranks; ++r) acc = acc + dequant(shard_codes[r], shard_scales[r], i);
+    uint16_t yi = orc_f32_to_bf16(acc);
+    y[i] = yi;
+    if (e) e[i] = orc_bf16_to_f32(yi) - acc;
+  }
+}
+
+int orc_rs_call(int nranks, int rank, int64_t n, const uint16_t* x, float* m_fast,
+                float* m_slow, const uint8_t* const* recv_codes, const float* const* recv_scales,
+                uint8_t* send_codes, float* send_scales, uint16_t* y_own, int comp) {
+  if (!shape_ok(nranks, n) || rank < 0 || rank >= nranks) return -1;
+  int64_t C = n / nranks;
+  uint8_t* codes1 = malloc((size_t)(n / 2));
+  float* scales1 = malloc((size_t)(n / ORC_GROUP) * sizeof(float));
+  float* e = malloc((size_t)C * sizeof(float));
+  if (!codes1 || !scales1 || !e) {
+    free(codes1); free(scales1); free(e);
+    return -1;
+  }
+  orc_encode(n, x, m_fast, m_slow, codes1, scales1, NULL, comp);
+  for (int j = 0; j < nranks; ++j) {
+    if (j == rank) continue;
+    memcpy(send_codes + j * C / 2, codes1 + j * C / 2, (size_t)(C / 2));
+    memcpy(send_scales + j * C / ORC_GROUP, scales1 + j * C / ORC_GROUP,
+           (size_t)(C / ORC_GROUP) * sizeof(float));
+  }
+  const uint8_t* sc[ORC_MAX_RANKS];
+  const float* ss[ORC_MAX_RANKS];
+  for (int q = 0; q < nranks; ++q) {
+    sc[q] = (q == rank) ? codes1 + rank * C / 2 : recv_codes[q];
+    ss[q] = (q == rank) ? scales1 + rank * C / ORC_GROUP : recv_scales[q];
+  }
+  orc_reduce_chunk_sum(nranks, C, sc, ss, y_own, e);
+  if (comp) orc_update(n, nranks, rank, x, m_fast, m_slow, codes1, scales1, e, NULL);
+  free(codes1); free(scales1); free(e);
+  return 0;
+}
+
+int orc_rs_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const* m_fast,
+                    float* const* m_slow, uint16_t* y, float* const* xp_out,
+                    float* const* r_out, int comp) {
+  if (!shape_ok(nranks, n)) return -1;
+  int64_t C = n / nranks;
+  uint8_t* codes1[ORC_MAX_RANKS] = {0};
+  float* scales1[ORC_MAX_RANKS] = {0};
+  float* e = malloc((size_t)n * sizeof(float));
+  int ok = e != NULL;
+  for (int p = 0; p < nranks && ok; ++p) {
+    codes1[p] = malloc((size_t)(n / 2));
+    scales1[p] = malloc((size_t)(n / ORC_GROUP) * sizeof(float));
+    ok = codes1[p] && scales1[p];
+  }
+  if (ok) {
+    for (int p = 0; p < nranks; ++p)
+      orc_encode(n, xs[p], comp ? m_fast[p] : NULL, comp ? m_slow[p] : NULL, codes1[p],
+                 scales1[p], xp_out ? xp_out[p] : NULL, comp);
+    for (int j = 0; j < nranks; ++j) {
+      const uint8_t* sc[ORC_MAX_RANKS];
+      const float* ss[ORC_MAX_RANKS];
+      for (int q = 0; q < nranks; ++q) {
+        sc[q] = codes1[q] + j * C / 2;
+        ss[q] = scales1[q] + j * C / ORC_GROUP;
+      }
+      orc_reduce_chunk_sum(nranks, C, sc, ss, y + j * C, e + j * C);
+    }
+    if (comp)
+      for (int p = 0; p < nranks; ++p)
+        orc_update(n, nranks, p, xs[p], m_fast[p], m_slow[p], codes1[p], scales1[p],
+                   e + p * C, r_out ? r_out[p] : NULL);
+  }
+  for (int p = 0; p < nranks; ++p) {
+    free(codes1[p]);
+    free(scales1[p]);
+  }
+  free(e);
+  return ok ? 0 : -1;
+}

@@ -101,6 +101,30 @@ int orc_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const*
                  uint8_t* const* codes1, float* const* scales1, float* const* xp,
                  float* const* r, int comp);
 
+/* ---- reduce-scatter only (the sequence-parallel variant) -------------------
+ * The pages name the reduce-scatter of sequence parallelism as a next target
+ * ("Tensor-parallel traffic drops to 4 bits", Perspective).  Reading: the
+ * entry pass is unchanged; the owner of chunk j sums the P stage-1 shards in
+ * rank order and outputs the sum as bf16 directly (no second quantization:
+ * each value is quantized once); the rounding of that output, e = f32(y) - S,
+ * plays the part of e2 in the residual. */
+
+/* S = d_0 + ... + d_{P-1}; y = bf16(S); e = f32(y) - S (e nullable). */
+void orc_reduce_chunk_sum(int nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
+                          const float* const* shard_scales, uint16_t* y, float* e);
+
+/* Rank mode: writes send_* for every chunk except `rank`, y_own[n/P] (the
+ * reduced own chunk) and updates the state when comp != 0.  Returns 0 or -1. */
+int orc_rs_call(int nranks, int rank, int64_t n, const uint16_t* x, float* m_fast,
+                float* m_slow, const uint8_t* const* recv_codes, const float* const* recv_scales,
+                uint8_t* send_codes, float* send_scales, uint16_t* y_own, int comp);
+
+/* All P ranks: y[n] holds chunk j as reduced by rank j.  Optional per-rank
+ * xp[p] and r[p] (nullable).  Returns 0 or -1. */
+int orc_rs_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const* m_fast,
+                    float* const* m_slow, uint16_t* y, float* const* xp, float* const* r,
+                    int comp);
+
 #ifdef __cplusplus
 }
 #endif

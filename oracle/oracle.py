@@ -57,6 +57,11 @@ def _load():
                                _vp, _vp, _vp, _vp, _vp, C.c_int]),
         "orc_simulate": (C.c_int, [C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, C.c_int]),
+        "orc_reduce_chunk_sum": (None, [C.c_int, C.c_int64, _vp, _vp, _vp, _vp]),
+        "orc_rs_call": (C.c_int, [C.c_int, C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, C.c_int]),
+        "orc_rs_simulate": (C.c_int, [C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      C.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -225,6 +230,53 @@ def simulate(xs, m_fast=None, m_slow=None, comp: bool = True, want_detail: bool 
     if rc != 0:
         raise ValueError("orc_simulate rejected its arguments")
     out = dict(codes2=codes2, scales2=scales2, y=y)
+    if det:
+        out.update(det)
+    return out
+
+
+# ---- reduce-scatter only ----------------------------------------------------------
+
+def reduce_chunk_sum(shard_codes, shard_scales, chunk_n: int):
+    """Rank-order sum of P shards output as bf16. Returns (y_bf16, e)."""
+    y = np.zeros(chunk_n, np.uint16)
+    e = np.zeros(chunk_n, np.float32)
+    lib().orc_reduce_chunk_sum(len(shard_codes), chunk_n, _ptr_array(shard_codes),
+                               _ptr_array(shard_scales), _p(y), _p(e))
+    return y, e
+
+
+def rs_call(nranks: int, rank: int, x, m_fast, m_slow, recv_codes, recv_scales, comp: bool = True):
+    """Rank-mode reduce-scatter call.  Returns dict(send_codes, send_scales, y_own)."""
+    n = x.size
+    Cn = n // nranks
+    send_codes = np.zeros(n // 2, np.uint8)
+    send_scales = np.zeros(n // GROUP, np.float32)
+    y_own = np.zeros(Cn, np.uint16)
+    rc = lib().orc_rs_call(nranks, rank, n, _p(x), _p(m_fast), _p(m_slow), _ptr_array(recv_codes),
+                           _ptr_array(recv_scales), _p(send_codes), _p(send_scales), _p(y_own),
+                           int(bool(comp)))
+    if rc != 0:
+        raise ValueError("orc_rs_call rejected its arguments")
+    return dict(send_codes=send_codes, send_scales=send_scales, y_own=y_own)
+
+
+def rs_simulate(xs, m_fast=None, m_slow=None, comp: bool = True, want_detail: bool = False):
+    """All P ranks' reduce-scatter call: y[n] holds chunk j as reduced by rank j."""
+    P = len(xs)
+    n = xs[0].size
+    y = np.zeros(n, np.uint16)
+    det = None
+    if want_detail:
+        det = dict(xp=[np.zeros(n, np.float32) for _ in range(P)],
+                   r=[np.zeros(n, np.float32) for _ in range(P)])
+    rc = lib().orc_rs_simulate(P, n, _ptr_array(xs), _ptr_array(m_fast) if comp else None,
+                               _ptr_array(m_slow) if comp else None, _p(y),
+                               _ptr_array(det["xp"]) if det else None,
+                               _ptr_array(det["r"]) if det else None, int(bool(comp)))
+    if rc != 0:
+        raise ValueError("orc_rs_simulate rejected its arguments")
+    out = dict(y=y)
     if det:
         out.update(det)
     return out

@@ -25,7 +25,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("echo_state_init", "echo_encode", "echo_reduce_shard", "echo_decode",
                  "echo_update", "echo_call", "echo_call_entry", "echo_call_reduce",
-                 "echo_call_exit", "echo_call_plain", "echo_get_config", "echo_status_string",
+                 "echo_call_exit", "echo_call_plain", "echo_reduce_shard_sum", "echo_rs_reduce",
+                 "echo_rs_call", "echo_get_config", "echo_status_string",
                  "echo_version"):
         assert want in names
 
@@ -164,3 +165,16 @@ def test_call_plain_rejections():
     assert rc(B.echo_call_plain, P, 1, 3 * A, bad, recv_s, gath_c, gath_s, *outs, n) == -1
     assert rc(B.echo_call_plain, P, 1, 3 * A, recv_c, recv_s, gath_c, gath_s, 50 * A, 51 * A,
               52 * A, 53 * A, 3 * A + 32, n) == -6
+
+
+def test_reduce_scatter_rejections():
+    P, n = 4, 4096
+    s4 = st(n=n, P=P, rank=2)
+    recv_c = [10 * A + k * A for k in range(P)]
+    recv_s = [20 * A + k * A for k in range(P)]
+    assert rc(B.echo_reduce_shard_sum, [3 * A, 4 * A], [5 * A, 6 * A], 7 * A, None, 100) == -2
+    assert rc(B.echo_reduce_shard_sum, [3 * A, 4 * A], [5 * A, 6 * A], 4 * A, None, 256) == -6
+    assert rc(B.echo_rs_reduce, s4, 3 * A, recv_c, recv_s, None) == -1
+    assert rc(B.echo_rs_reduce, s4, 3 * A, recv_c, recv_s, 3 * A + 4096) == -6  # y_own inside x
+    assert rc(B.echo_rs_call, s4, 3 * A, recv_c, recv_s, 50 * A, 51 * A, 52 * A + 2) == -3
+    assert rc(B.echo_rs_call, s4, 3 * A, recv_c, recv_s, 50 * A, 51 * A, A) == -6  # y_own over m_fast

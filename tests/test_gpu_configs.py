@@ -240,3 +240,37 @@ def test_config_1gb_rank_mode():
             say(f"1gb: call {call} windows ok")
     run.check_exit_full("call 22")
     run.check_message_properties("call 22")
+
+
+@pytest.mark.parametrize("a", [1.0, 1.1])
+def test_deep_chain_on_the_gpu(a):
+    """The deep chain h <- a h + y run through the GPU (P = 8 ranks simulated),
+    every call bit-identical to the oracle: bounded at sqrt(2.289) times one
+    call's injected error for the identity map, geometric growth for a = 1.1."""
+    P, n, L = 8, 8 * 128 * 4, 48
+    rng = np.random.default_rng(17)
+    mf = [np.zeros(n, np.float32) for _ in range(P)]
+    ms = [np.zeros(n, np.float32) for _ in range(P)]
+    ranks = [g.GpuRank(np.zeros(n, np.uint16), mf[p], ms[p], P, p) for p in range(P)]
+    h = np.zeros(n)
+    H = np.zeros(n)
+    dev, inj = [], []
+    for call in range(L):
+        xs = [I.to_bf16_bits(rng.standard_normal(n)) for _ in range(P)]
+        g.gpu_simulate_call(ranks, xs)
+        want = orc.simulate(xs, mf, ms, want_detail=True)
+        y_gpu = g.host(ranks[0].y, np.uint16)
+        g.eq(y_gpu, want["y"], f"chain call {call} y")
+        g.eq(g.host(ranks[3].mf, np.float32), mf[3], f"chain call {call} m_fast")
+        y = (y_gpu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        xsum = np.sum([(x.astype(np.uint32) << 16).view(np.float32).astype(np.float64) for x in xs], axis=0)
+        inj.append(np.sqrt(np.mean((y - np.sum(want["xp"], axis=0, dtype=np.float64)) ** 2)))
+        h = a * h + y
+        H = a * H + xsum
+        dev.append(np.sqrt(np.mean((h - H) ** 2)))
+    dev = np.array(dev) / np.mean(inj)
+    if a == 1.0:
+        assert abs(dev[-8:].mean() - np.sqrt(2.2889)) < 0.2, dev[-8:]
+    else:
+        rate = np.polyfit(np.arange(24, L), np.log(dev[24:]), 1)[0]
+        assert abs(rate - np.log(a)) < 0.03, rate

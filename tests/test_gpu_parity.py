@@ -493,3 +493,116 @@ def test_requantizer_decision_boundaries(ulps):
     eq(g.host(out_c, np.uint8), wc, "codes2")
     eq(g.host(out_y, np.uint16), wy, "y")
     eq(g.host(out_e2, np.float32), we, "e2")
+
+
+# ---- reduce-scatter only ----------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("k", [1, 5, 129])
+def test_reduce_shard_sum(P, k):
+    g = gu()
+    cn = 128 * k
+    msgs = [I.int4_message(cn, I.stream_key("rss", P, k, q), zero_group_frac=0.05, any_byte=(q % 2 == 1))
+            for q in range(P)]
+    y, e = g.empty_bf16(cn), g.empty_f32(cn)
+    B.echo_reduce_shard_sum([g.dev(c) for c, _ in msgs], [g.dev(s) for _, s in msgs], y, e, chunk_n=cn)
+    wy, we = orc.reduce_chunk_sum([c for c, _ in msgs], [s for _, s in msgs], cn)
+    eq(g.host(y, np.uint16), wy, "y")
+    eq(g.host(e, np.float32), we, "e")
+
+
+class RsCase(RankCase):
+    def __init__(self, P, rank, k, seed):
+        super().__init__(P, rank, k, seed)
+        self.y_own = gu().empty_bf16(self.Cn)
+
+    def gpu_rs(self, xd):
+        B.echo_rs_call(self.st, xd, self.slot(self.recv_d, 0), self.slot(self.recv_d, 1),
+                       self.send_c, self.send_s, self.y_own)
+
+    def oracle_rs(self, x):
+        return orc.rs_call(self.P, self.rank, x, self.mf, self.ms, self.slot(self.recv, 0),
+                           self.slot(self.recv, 1))
+
+    def check_rs(self, want):
+        g = gu()
+        P, r, Cn = self.P, self.rank, self.Cn
+        sc = g.host(self.send_c, np.uint8)
+        ss = g.host(self.send_s, np.float32)
+        for j in range(P):
+            cs = slice(j * Cn // 2, (j + 1) * Cn // 2)
+            gs = slice(j * Cn // 128, (j + 1) * Cn // 128)
+            if j == r:
+                assert np.all(sc[cs] == 0xAB) and np.all(ss[gs] == -3.0)
+            else:
+                eq(sc[cs], want["send_codes"][cs], f"send codes chunk {j}")
+                eq(ss[gs], want["send_scales"][gs], f"send scales chunk {j}")
+        eq(g.host(self.y_own, np.uint16), want["y_own"], "y_own")
+        eq(g.host(self.mfd, np.float32), self.mf, "m_fast")
+        eq(g.host(self.msd, np.float32), self.ms, "m_slow")
+
+
+@pytest.mark.parametrize("P,rank,k", [(1, 0, 2), (2, 1, 3), (3, 0, 5), (8, 0, 16), (8, 7, 33), (16, 4, 3)])
+def test_rs_call_rank_mode(P, rank, k):
+    g = gu()
+    case = RsCase(P, rank, k, seed=400 + P * 10 + rank)
+    for call in range(3):
+        x = x_of(case.n, 800 + call + k)
+        case.gpu_rs(g.dev(x))
+        case.check_rs(case.oracle_rs(x))
+
+
+@pytest.mark.parametrize("P,rank,k", [(8, 5, 9), (4, 0, 3)])
+def test_rs_fused_equals_unfused(P, rank, k):
+    """echo_rs_call == echo_encode + echo_reduce_shard_sum (own slot = own
+    stage-1 chunk) + echo_update, bit for bit, and the phased form too."""
+    g = gu()
+    a = RsCase(P, rank, k, seed=9)
+    b = RsCase(P, rank, k, seed=9)
+    c = RsCase(P, rank, k, seed=9)
+    n, Cn = a.n, a.Cn
+    for call in range(3):
+        xd = g.dev(x_of(n, 60 + call))
+        a.gpu_rs(xd)
+        codes1, scales1 = g.empty_u8(n // 2), g.empty_f32(n // 128)
+        B.echo_encode(b.st, xd, codes1, scales1)
+        sh_c = [codes1[rank * Cn // 2:(rank + 1) * Cn // 2] if q == rank else b.recv_d[q][0] for q in range(P)]
+        sh_s = [scales1[rank * Cn // 128:(rank + 1) * Cn // 128] if q == rank else b.recv_d[q][1]
+                for q in range(P)]
+        e = g.empty_f32(Cn)
+        B.echo_reduce_shard_sum(sh_c, sh_s, b.y_own, e, chunk_n=Cn)
+        B.echo_update(b.st, xd, codes1, scales1, e)
+        B.echo_call_entry(c.st, xd, c.send_c, c.send_s)
+        B.echo_rs_reduce(c.st, xd, c.slot(c.recv_d, 0), c.slot(c.recv_d, 1), c.y_own)
+        for other in (b, c):
+            eq(g.host(a.y_own, np.uint16), g.host(other.y_own, np.uint16), "y_own")
+            eq(g.host(a.mfd, np.float32), g.host(other.mfd, np.float32), "m_fast")
+            eq(g.host(a.msd, np.float32), g.host(other.msd, np.float32), "m_slow")
+
+
+@pytest.mark.parametrize("P,k,calls", [(3, 2, 3), (8, 4, 4)])
+def test_rs_full_simulation(P, k, calls):
+    """P logical ranks, each running echo_rs_call on the others' stage-1
+    chunks of its own chunk, against the oracle's reduce-scatter simulation."""
+    g = gu()
+    n = P * 128 * k
+    Cn = n // P
+    mf = [np.zeros(n, np.float32) for _ in range(P)]
+    ms = [np.zeros(n, np.float32) for _ in range(P)]
+    ranks = [g.GpuRank(np.zeros(n, np.uint16), mf[p], ms[p], P, p) for p in range(P)]
+    y_own = [g.empty_bf16(Cn) for _ in range(P)]
+    for call in range(calls):
+        xs = [x_of(n, 3000 + 10 * call + p) for p in range(P)]
+        for r, x in zip(ranks, xs):
+            r.x.copy_(g.dev(x))
+            B.echo_encode(r.st, r.x, r.codes1, r.scales1)
+        for p, r in enumerate(ranks):
+            recv_c = [None if q == p else ranks[q].codes1[p * Cn // 2:(p + 1) * Cn // 2] for q in range(P)]
+            recv_s = [None if q == p else ranks[q].scales1[p * Cn // 128:(p + 1) * Cn // 128] for q in range(P)]
+            B.echo_rs_call(r.st, r.x, recv_c, recv_s, r.send_codes, r.send_scales, y_own[p])
+        torch.cuda.synchronize()
+        want = orc.rs_simulate(xs, mf, ms)
+        for p, r in enumerate(ranks):
+            eq(g.host(y_own[p], np.uint16), want["y"][p * Cn:(p + 1) * Cn], f"call {call} y rank {p}")
+            eq(g.host(r.mf, np.float32), mf[p], f"call {call} m_fast rank {p}")
+            eq(g.host(r.ms, np.float32), ms[p], f"call {call} m_slow rank {p}")
