@@ -34,6 +34,7 @@ extern "C" {
 #define ORC_BETA_SLOW 0.875f /* slow average: m <- 0.875 m + 0.125 r */
 #define ORC_ALPHA_SLOW 0.125f
 #define ORC_MAX_RANKS 16
+#define ORC_QMAX8 127        /* 8-bit promotion of a call: codes in [-127, 127] */
 
 /* Number of values the quantizer has processed, per stage (1 = entry,
  * 2 = reduce).  Used by the "quantized at most twice" pin. */
@@ -48,11 +49,21 @@ float orc_bf16_to_f32(uint16_t h);
  * amax = max |v|, s = amax / QMAX, q = clamp(rint(v / s), -QMAX, QMAX);
  * s == 0 (all-zero group, or amax / QMAX underflowing) gives codes 0. */
 void orc_quantize_group(const float* v, int len, int8_t* q, float* scale, int stage);
+/* The same with an explicit code range (7 for 4-bit, 127 for 8-bit codes). */
+void orc_quantize_group_q(const float* v, int len, int qmax, int8_t* q, float* scale,
+                          int stage);
 
 /* Nibble packing: byte k holds element 2k in its low nibble and element
  * 2k+1 in its high nibble, both two's complement.  n must be even. */
 void orc_pack(const int8_t* q, int64_t n, uint8_t* codes);
 void orc_unpack(const uint8_t* codes, int64_t n, int8_t* q);
+
+/* Code width `bits` (4 or 8) of every message below: 4 -> packed nibbles as
+ * above, codes in [-7, 7]; 8 -> one two's-complement byte per element, codes
+ * in [-127, 127] (the pages promote the first half of the layers to 8 bits in
+ * serving, "Tensor-parallel traffic drops to 4 bits", Perspective). */
+void orc_pack_codes(const int8_t* q, int64_t n, uint8_t* codes, int bits);
+void orc_unpack_codes(const uint8_t* codes, int64_t n, int8_t* q, int bits);
 
 /* Fold r into both averages: m_f <- B_F m_f + A_F r, m_s <- B_S m_s + A_S r. */
 void orc_ema_refresh(int64_t n, float* m_fast, float* m_slow, const float* r);
@@ -61,24 +72,24 @@ void orc_ema_refresh(int64_t n, float* m_fast, float* m_slow, const float* r);
  * (or x' = f32(x) when comp == 0), then group-quantize x'.  The state is
  * read, not written.  xp_out (nullable) receives x'. */
 void orc_encode(int64_t n, const uint16_t* x, const float* m_fast, const float* m_slow,
-                uint8_t* codes, float* scales, float* xp_out, int comp);
+                uint8_t* codes, float* scales, float* xp_out, int comp, int bits);
 
 /* Reduce one chunk of chunk_n elements from P shards: S = d_0 + ... + d_{P-1}
  * in rank order, requantize S, y = bf16(code2 * s2), e2 = f32(y) - S.
  * y and e2 are nullable. */
 void orc_reduce_chunk(int nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
                       const float* const* shard_scales, uint8_t* codes2, float* scales2,
-                      uint16_t* y, float* e2);
+                      uint16_t* y, float* e2, int bits);
 
 /* Exit pass: y = bf16(code * scale). */
-void orc_decode(int64_t n, const uint8_t* codes, const float* scales, uint16_t* y);
+void orc_decode(int64_t n, const uint8_t* codes, const float* scales, uint16_t* y, int bits);
 
 /* Update: recompute x' from the pre-call state, d1 from codes1/scales1,
  * r = d1 - x' (+ e2_own on the chunk [rank*n/P, (rank+1)*n/P)), refresh both
  * averages in place.  r_out (nullable) receives r. */
 void orc_update(int64_t n, int nranks, int rank, const uint16_t* x, float* m_fast,
                 float* m_slow, const uint8_t* codes1, const float* scales1,
-                const float* e2_own, float* r_out);
+                const float* e2_own, float* r_out, int bits);
 
 /* One call in rank mode (rank p of P): incoming shards recv_*[q] (q != p,
  * each covering chunk p) and gathered outputs gath_*[j] (j != p, each
@@ -89,7 +100,7 @@ int orc_call(int nranks, int rank, int64_t n, const uint16_t* x, float* m_fast,
              float* m_slow, const uint8_t* const* recv_codes, const float* const* recv_scales,
              const uint8_t* const* gath_codes, const float* const* gath_scales,
              uint8_t* send_codes, float* send_scales, uint8_t* own_codes2, float* own_scales2,
-             uint16_t* y, int comp);
+             uint16_t* y, int comp, int bits);
 
 /* One call with all P ranks simulated: xs[p], m_fast[p], m_slow[p] per rank.
  * Writes the all-gathered codes2/scales2 and the output y (identical on
@@ -99,7 +110,7 @@ int orc_call(int nranks, int rank, int64_t n, const uint16_t* x, float* m_fast,
 int orc_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const* m_fast,
                  float* const* m_slow, uint8_t* codes2, float* scales2, uint16_t* y,
                  uint8_t* const* codes1, float* const* scales1, float* const* xp,
-                 float* const* r, int comp);
+                 float* const* r, int comp, int bits);
 
 /* ---- reduce-scatter only (the sequence-parallel variant) -------------------
  * The pages name the reduce-scatter of sequence parallelism as a next target
@@ -111,19 +122,19 @@ int orc_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const*
 
 /* S = d_0 + ... + d_{P-1}; y = bf16(S); e = f32(y) - S (e nullable). */
 void orc_reduce_chunk_sum(int nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
-                          const float* const* shard_scales, uint16_t* y, float* e);
+                          const float* const* shard_scales, uint16_t* y, float* e, int bits);
 
 /* Rank mode: writes send_* for every chunk except `rank`, y_own[n/P] (the
  * reduced own chunk) and updates the state when comp != 0.  Returns 0 or -1. */
 int orc_rs_call(int nranks, int rank, int64_t n, const uint16_t* x, float* m_fast,
                 float* m_slow, const uint8_t* const* recv_codes, const float* const* recv_scales,
-                uint8_t* send_codes, float* send_scales, uint16_t* y_own, int comp);
+                uint8_t* send_codes, float* send_scales, uint16_t* y_own, int comp, int bits);
 
 /* All P ranks: y[n] holds chunk j as reduced by rank j.  Optional per-rank
  * xp[p] and r[p] (nullable).  Returns 0 or -1. */
 int orc_rs_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const* m_fast,
                     float* const* m_slow, uint16_t* y, float* const* xp, float* const* r,
-                    int comp);
+                    int comp, int bits);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,28 @@ CASES = [
          v=pad([-8 * TINY, 4 * TINY, TINY]), scale=TINY, codes=pad([-7, 4, 1])),
 ]
 
+CASES8 = [
+    dict(name="8-bit: unit scale, ties to even",
+         why="amax = 127 so s = 127/127 = 1 exactly and v/s = v; rint sends 2.5->2, "
+             "3.5->4, 126.5->126, -126.5->-126, -0.5->0, 64.5->64",
+         v=pad([127.0, 2.5, 3.5, 126.5, -126.5, -0.5, 64.5, -100.0]),
+         scale=1.0, codes=pad([127, 2, 4, 126, -126, 0, 64, -100])),
+    dict(name="8-bit: scale 2",
+         why="amax = 254, s = 2; -254/2 = -127, 3/2 = 1.5 -> 2, 5/2 = 2.5 -> 2, 253/2 = 126.5 -> 126",
+         v=pad([-254.0, 3.0, 5.0, 253.0]), scale=2.0, codes=pad([-127, 2, 2, 126])),
+    dict(name="8-bit: amax/127 underflows to zero",
+         why="amax = 63 * 2^-149; 63/127 < 1/2 of the smallest denormal rounds to 0",
+         v=pad([63 * TINY, -TINY]), scale=0.0, codes=pad([])),
+    dict(name="8-bit: denormal scale, clamp at -127",
+         why="amax = 128 * 2^-149; 128/127 rounds to s = 2^-149, so -128 clamps to -127",
+         v=pad([-128 * TINY, 5 * TINY]), scale=TINY, codes=pad([-127, 5])),
+]
+
+PACK8 = [
+    dict(q=[-1, 127, -127, 0], bytes=[0xFF, 0x7F, 0x81, 0x00],
+         why="one two's-complement byte per code"),
+]
+
 PACK = [
     dict(q=[1, -1], byte=0xF1, why="low nibble 0x1, high nibble -1 = 0xF"),
     dict(q=[-7, 7], byte=0x79, why="-7 = 0x9 low, 7 high"),
@@ -79,7 +101,9 @@ def main():
                "'Echo: Error-Compensated 4-Bit Tensor-Parallel Communication', Abstract)",
         quantizer=[dict(name=c["name"], why=c["why"], v=[float(t).hex() for t in c["v"]],
                         scale=float(c["scale"]).hex(), codes=c["codes"]) for c in CASES],
-        pack=PACK, bf16=BF16)
+        quantizer8=[dict(name=c["name"], why=c["why"], v=[float(t).hex() for t in c["v"]],
+                         scale=float(c["scale"]).hex(), codes=c["codes"]) for c in CASES8],
+        pack=PACK, pack8=PACK8, bf16=BF16)
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantizer_hand_cases.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)

@@ -36,6 +36,20 @@ def test_hand_quantizer_cases(hand):
         assert q.tolist() == case["codes"], case["name"]
 
 
+def test_hand_quantizer_cases_8bit(hand):
+    for case in hand["quantizer8"]:
+        v = np.array([float.fromhex(t) for t in case["v"]], dtype=np.float32)
+        q, s = orc.quantize_group_q(v, 127)
+        assert s == float.fromhex(case["scale"]), case["name"]
+        assert q.tolist() == case["codes"], case["name"]
+
+
+def test_hand_byte_codes_8bit(hand):
+    for case in hand["pack8"]:
+        assert orc.pack_codes(np.array(case["q"], np.int8), bits=8).tolist() == case["bytes"]
+        assert orc.unpack_codes(np.array(case["bytes"], np.uint8), 4, bits=8).tolist() == case["q"]
+
+
 def test_hand_pack_cases(hand):
     for case in hand["pack"]:
         assert orc.pack(np.array(case["q"], np.int8)).tolist() == [case["byte"]], case["why"]
@@ -93,37 +107,46 @@ def _groups(rng):
     yield (rng.integers(-3, 4, 128) * 2.0 ** -140).astype(np.float32)  # denormal scale
 
 
-def test_quantizer_is_nearest_code_exact_arithmetic():
-    """Every code is the exact nearest of the 15 codes to v (ties to the even
-    code), with s the correctly rounded binary32 value of amax/7; values
-    whose v/s lies within 2^-20 of a half-integer are decided by the binary32
-    quotient and checked against numpy's IEEE division instead."""
-    rng = np.random.default_rng(1)
+@pytest.mark.parametrize("qmax", [7, 127])
+def test_quantizer_is_nearest_code_exact_arithmetic(qmax):
+    """Every code is the exact nearest of the 2*qmax+1 codes to v (ties to the
+    even code), with s the correctly rounded binary32 value of amax/qmax;
+    values whose v/s lies within 2^-20 of a half-integer are decided by the
+    binary32 quotient and checked against numpy's IEEE division instead."""
+    rng = np.random.default_rng(1 + qmax)
     n_checked = n_boundary = 0
-    for _ in range(20):
+    for _ in range(20 if qmax == 7 else 6):
         for v in _groups(rng):
             v = np.ascontiguousarray(v, np.float32)
-            q, s = orc.quantize_group(v)
+            if qmax == 127:
+                v = v * np.float32(127.0 / 7.0)  # keep the half-integer family on the grid
+                v = np.ascontiguousarray(v, np.float32)
+            q, s = orc.quantize_group_q(v, qmax)
             amax = Fraction(float(np.max(np.abs(v))))
             if s == 0.0:
-                # all-zero group, or amax/7 below half the smallest denormal
-                assert amax / 7 <= Fraction(2.0 ** -150)
+                # all-zero group, or amax/qmax below half the smallest denormal
+                assert amax / qmax <= Fraction(2.0 ** -150)
                 assert not q.any()
                 continue
-            assert _is_nearest_f32(s, amax / 7)
+            assert _is_nearest_f32(s, amax / qmax)
             S = Fraction(s)
             for vi, qi in zip(v.tolist(), q.tolist()):
                 t = Fraction(vi) / S
                 frac = t - (t.numerator // t.denominator)
                 if abs(frac - Fraction(1, 2)) < Fraction(1, 1 << 20):
                     n_boundary += 1
-                    ref = np.clip(np.rint(np.float32(vi) / np.float32(s)), -7, 7)
+                    ref = np.clip(np.rint(np.float32(vi) / np.float32(s)), -qmax, qmax)
                     assert qi == int(ref)
                     continue
-                cands = sorted(range(-7, 8), key=lambda c: (abs(Fraction(vi) - c * S), c % 2))
+                if qmax == 7:  # brute force over the whole code set
+                    pool = range(-qmax, qmax + 1)
+                else:  # the nearest code is one of the two integers around v/s, clamped
+                    lo = max(-qmax, min(qmax, t.numerator // t.denominator))
+                    pool = {lo, max(-qmax, min(qmax, lo + 1))}
+                cands = sorted(pool, key=lambda c: (abs(Fraction(vi) - c * S), c % 2))
                 assert qi == cands[0], (vi, s, qi, cands[:2])
                 n_checked += 1
-    assert n_checked > 10000 and n_boundary > 50
+    assert n_checked > 3000 and n_boundary > 20
 
 
 def test_quantizer_error_bound():
