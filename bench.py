@@ -30,9 +30,9 @@ METRIC = "GB/s of bf16 payload through fused Echo rank pipeline @1GB msg; % HBM 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published peak
 
 
-def bytes_per_element(P: int) -> dict:
+def bytes_per_element(P: int, bits: int = 4) -> dict:
     """Algorithmic HBM bytes per element of each kernel's range."""
-    code = 0.5 + 4.0 / 128.0  # packed nibble + share of the fp32 group scale
+    code = bits / 8.0 + 4.0 / 128.0  # code + share of the fp32 group scale
     return {
         "entry": 2 + 8 + 8 + code,             # x, 2 averages in, 2 out, send message
         "reduce": 2 + 8 + 8 + 2 + code * P,    # x, averages in/out, y, P-1 shards in + codes2 out
@@ -48,8 +48,8 @@ def rs_bytes(N: int, P: int) -> float:
     return (N - C) * bytes_per_element(P)["entry"] + C * (2 + 16 + code * (P - 1) + 2)
 
 
-def step_bytes(N: int, P: int) -> float:
-    b = bytes_per_element(P)
+def step_bytes(N: int, P: int, bits: int = 4) -> float:
+    b = bytes_per_element(P, bits)
     C = N // P
     return (N - C) * b["entry"] + C * b["reduce"] + (N - C) * b["exit"]
 
@@ -238,9 +238,34 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         B.echo_rs_call(st, xd, rc_, rs_, send_c, send_s, y_own, main)
         if e: e[1].record(main)
 
+    # the 8-bit promotion of a call: the same call with one byte per code
+    # (seeded random 8-bit messages drawn on the device: only the bytes moved
+    # matter for the timing)
+    g8 = torch.Generator(device=y.device)
+    g8.manual_seed(8)
+
+    def msg8():
+        c = torch.randint(0, 256, (C,), device=y.device, generator=g8, dtype=torch.uint8)
+        c[c == 0x80] = 0x7F
+        sc = torch.rand(C // 128, device=y.device, generator=g8) * 0.01 + 0.001
+        return c, sc
+
+    m8 = [None if q == rank else msg8() for q in range(P)]
+    rc8 = [None if m is None else m[0] for m in m8]
+    rs8 = [None if m is None else m[1] for m in m8]
+    send_c8 = torch.empty(N, dtype=torch.uint8, device=y.device)
+    own_c8 = torch.empty(C, dtype=torch.uint8, device=y.device)
+
+    def b_call8(e=None):
+        st.bits = 8
+        if e: e[0].record(main)
+        B.echo_call(st, xd, rc8, rs8, rc8, rs8, send_c8, send_s, own_c8, own_s, y, main)
+        if e: e[1].record(main)
+        st.bits = 4
+
     out = {}
     for name, body in (("gemm", b_gemm), ("fused", b_fused), ("plain", b_plain), ("split", b_split),
-                       ("update_alone", b_update), ("rs", b_rs)):
+                       ("update_alone", b_update), ("rs", b_rs), ("call8", b_call8)):
         wall, first = timed(body)
         out[name] = (wall, first)
     torch.cuda.synchronize()
@@ -253,6 +278,8 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         "update_alone_ms": round(out["update_alone"][1], 4),
         "layer_ms": {"fused+matmul": round(out["fused"][0], 4), "plain+matmul": round(out["plain"][0], 4),
                      "split+matmul(update beside it)": round(out["split"][0], 4)},
+        "call_8bit_ms": round(out["call8"][1], 4),
+        "call_8bit_GBps": round(step_bytes(N, P, bits=8) / (out["call8"][1] * 1e-3) / 1e9, 1),
         "reduce_scatter_call_ms": round(out["rs"][1], 4),
         "reduce_scatter_GBps": round(rs_bytes(N, P) / (out["rs"][1] * 1e-3) / 1e9, 1),
         "compensation_on_critical_path_ms": {

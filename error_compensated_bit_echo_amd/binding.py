@@ -30,12 +30,13 @@ class EchoError(RuntimeError):
 
 class EchoStateC(C.Structure):
     _fields_ = [("m_fast", C.c_void_p), ("m_slow", C.c_void_p), ("n", C.c_int64),
-                ("nranks", C.c_int32), ("rank", C.c_int32)]
+                ("nranks", C.c_int32), ("rank", C.c_int32), ("bits", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class EchoConfigC(C.Structure):
     _fields_ = [("abi_version", C.c_int32), ("group", C.c_int32), ("qmax", C.c_int32),
-                ("max_ranks", C.c_int32), ("w_fast", C.c_float), ("w_slow", C.c_float),
+                ("qmax8", C.c_int32), ("max_ranks", C.c_int32), ("w_fast", C.c_float), ("w_slow", C.c_float),
                 ("beta_fast", C.c_float), ("alpha_fast", C.c_float), ("beta_slow", C.c_float),
                 ("alpha_slow", C.c_float), ("max_elements", C.c_int64)]
 
@@ -45,16 +46,16 @@ _pp = C.POINTER(C.c_void_p)
 _SIGNATURES = {
     "echo_state_init": [C.POINTER(EchoStateC), _vp, _vp, C.c_int64, C.c_int32, C.c_int32, _vp],
     "echo_encode": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp],
-    "echo_reduce_shard": [C.c_int32, C.c_int64, _pp, _pp, _vp, _vp, _vp, _vp, _vp],
-    "echo_decode": [C.c_int64, _vp, _vp, _vp, _vp],
+    "echo_reduce_shard": [C.c_int32, C.c_int64, C.c_int32, _pp, _pp, _vp, _vp, _vp, _vp, _vp],
+    "echo_decode": [C.c_int64, C.c_int32, _vp, _vp, _vp, _vp],
     "echo_update": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp, _vp],
     "echo_call_entry": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp],
     "echo_call_reduce": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp, _vp, _vp],
     "echo_call_exit": [C.POINTER(EchoStateC), _pp, _pp, _vp, _vp],
     "echo_call": [C.POINTER(EchoStateC), _vp, _pp, _pp, _pp, _pp, _vp, _vp, _vp, _vp, _vp, _vp],
-    "echo_call_plain": [C.c_int32, C.c_int32, C.c_int64, _vp, _pp, _pp, _pp, _pp, _vp, _vp, _vp,
-                        _vp, _vp, _vp],
-    "echo_reduce_shard_sum": [C.c_int32, C.c_int64, _pp, _pp, _vp, _vp, _vp],
+    "echo_call_plain": [C.c_int32, C.c_int32, C.c_int64, C.c_int32, _vp, _pp, _pp, _pp, _pp, _vp,
+                        _vp, _vp, _vp, _vp, _vp],
+    "echo_reduce_shard_sum": [C.c_int32, C.c_int64, C.c_int32, _pp, _pp, _vp, _vp, _vp],
     "echo_rs_reduce": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp],
     "echo_rs_call": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp, _vp, _vp],
     "echo_get_config": [C.POINTER(EchoConfigC)],
@@ -113,11 +114,21 @@ def _stream(stream):
 
 class EchoState:
     """Compensator state of one call sequence: two float32 averages of n
-    elements (caller-owned tensors), P ranks, this rank."""
+    elements (caller-owned tensors), P ranks, this rank, and the code width of
+    the next call's messages (`bits`, 4 or 8; may change from call to call)."""
 
-    def __init__(self, m_fast: torch.Tensor, m_slow: torch.Tensor, n: int, nranks: int, rank: int):
+    def __init__(self, m_fast: torch.Tensor, m_slow: torch.Tensor, n: int, nranks: int, rank: int,
+                 bits: int = 4):
         self.m_fast, self.m_slow = m_fast, m_slow  # keep the buffers alive
-        self.c = EchoStateC(_ptr(m_fast), _ptr(m_slow), int(n), int(nranks), int(rank))
+        self.c = EchoStateC(_ptr(m_fast), _ptr(m_slow), int(n), int(nranks), int(rank), int(bits), 0)
+
+    @property
+    def bits(self) -> int:
+        return self.c.bits
+
+    @bits.setter
+    def bits(self, value: int) -> None:
+        self.c.bits = int(value)
 
     @property
     def n(self) -> int:
@@ -132,10 +143,11 @@ class EchoState:
         return self.c.rank
 
 
-def echo_state_init(m_fast, m_slow, n, nranks, rank, stream=None) -> EchoState:
+def echo_state_init(m_fast, m_slow, n, nranks, rank, stream=None, bits: int = 4) -> EchoState:
     st = EchoState(m_fast, m_slow, n, nranks, rank)
     _check(lib.echo_state_init(C.byref(st.c), _ptr(m_fast), _ptr(m_slow), int(n), int(nranks),
                                int(rank), _stream(stream)), "echo_state_init")
+    st.bits = bits
     return st
 
 
@@ -145,19 +157,19 @@ def echo_encode(st: EchoState, x, codes, scales, stream=None) -> None:
 
 
 def echo_reduce_shard(shard_codes, shard_scales, out_codes, out_scales, out_y=None, out_e2=None,
-                      chunk_n=None, stream=None) -> None:
+                      chunk_n=None, stream=None, bits: int = 4) -> None:
     P = len(shard_codes)
     if chunk_n is None:
-        chunk_n = out_codes.numel() * 2
-    _check(lib.echo_reduce_shard(P, int(chunk_n), _ptrs(shard_codes), _ptrs(shard_scales),
+        chunk_n = out_codes.numel() * (1 if bits == 8 else 2)
+    _check(lib.echo_reduce_shard(P, int(chunk_n), int(bits), _ptrs(shard_codes), _ptrs(shard_scales),
                                  _ptr(out_codes), _ptr(out_scales), _ptr(out_y), _ptr(out_e2),
                                  _stream(stream)), "echo_reduce_shard")
 
 
-def echo_decode(codes, scales, y, n=None, stream=None) -> None:
+def echo_decode(codes, scales, y, n=None, stream=None, bits: int = 4) -> None:
     if n is None:
         n = y.numel()
-    _check(lib.echo_decode(int(n), _ptr(codes), _ptr(scales), _ptr(y), _stream(stream)),
+    _check(lib.echo_decode(int(n), int(bits), _ptr(codes), _ptr(scales), _ptr(y), _stream(stream)),
            "echo_decode")
 
 
@@ -193,20 +205,20 @@ def echo_call(st: EchoState, x, recv_codes, recv_scales, gath_codes, gath_scales
 
 def echo_call_plain(nranks, rank, x, recv_codes, recv_scales, gath_codes, gath_scales,
                     send_codes, send_scales, own_codes2, own_scales2, y, n=None,
-                    stream=None) -> None:
+                    stream=None, bits: int = 4) -> None:
     if n is None:
         n = x.numel()
-    _check(lib.echo_call_plain(int(nranks), int(rank), int(n), _ptr(x), _ptrs(recv_codes),
+    _check(lib.echo_call_plain(int(nranks), int(rank), int(n), int(bits), _ptr(x), _ptrs(recv_codes),
                                _ptrs(recv_scales), _ptrs(gath_codes), _ptrs(gath_scales),
                                _ptr(send_codes), _ptr(send_scales), _ptr(own_codes2),
                                _ptr(own_scales2), _ptr(y), _stream(stream)), "echo_call_plain")
 
 
 def echo_reduce_shard_sum(shard_codes, shard_scales, out_y, out_e2=None, chunk_n=None,
-                          stream=None) -> None:
+                          stream=None, bits: int = 4) -> None:
     if chunk_n is None:
         chunk_n = out_y.numel()
-    _check(lib.echo_reduce_shard_sum(len(shard_codes), int(chunk_n), _ptrs(shard_codes),
+    _check(lib.echo_reduce_shard_sum(len(shard_codes), int(chunk_n), int(bits), _ptrs(shard_codes),
                                      _ptrs(shard_scales), _ptr(out_y), _ptr(out_e2),
                                      _stream(stream)), "echo_reduce_shard_sum")
 

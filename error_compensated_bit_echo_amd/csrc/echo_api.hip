@@ -56,6 +56,11 @@ uint32_t blocks_for(uint64_t wave_steps) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+bool bits_ok(int32_t bits) { return bits == 4 || bits == 8; }
+
+// bytes of the codes of n elements: packed nibbles, or one byte per code
+int64_t code_bytes(int64_t n, int32_t bits) { return bits == 8 ? n : n / 2; }
+
 int check_ranks_shape(int64_t n, int32_t P) {
   if (P < 1 || P > ECHO_MAX_RANKS) return ECHO_ERR_RANKS;
   if (n <= 0 || n > ECHO_MAX_ELEMENTS || n % ((int64_t)P * ECHO_GROUP) != 0) return ECHO_ERR_SHAPE;
@@ -67,6 +72,7 @@ int check_state(const echo_state* st) {
   int rc = check_ranks_shape(st->n, st->nranks);
   if (rc) return rc;
   if (st->rank < 0 || st->rank >= st->nranks) return ECHO_ERR_RANKS;
+  if (!bits_ok(st->bits)) return ECHO_ERR_FORMAT;
   if (!aligned(st->m_fast, 16) || !aligned(st->m_slow, 16)) return ECHO_ERR_ALIGNMENT;
   return ECHO_SUCCESS;
 }
@@ -121,13 +127,16 @@ int launch_status() { return hipGetLastError() == hipSuccess ? ECHO_SUCCESS : EC
 constexpr int u_stage1(int mode) { return mode == kEntryPlain ? ECHO_U_PLAIN : kU1; }
 
 template <int MODE>
-int launch_stage1(const Stage1Args& a, hipStream_t s) {
+int launch_stage1(const Stage1Args& a, int bits, hipStream_t s) {
   constexpr int U = u_stage1(MODE);
   const uint64_t nslices = ((uint64_t)a.groups_work + 1) / 2;
   if (nslices == 0) return ECHO_SUCCESS;
   uint32_t blocks = blocks_for((nslices + U - 1) / U);
   if (MODE == kUpdate && blocks > (uint32_t)ECHO_UPDATE_MAX_BLOCKS) blocks = ECHO_UPDATE_MAX_BLOCKS;
-  hipLaunchKernelGGL((k_stage1<MODE, U>), dim3(blocks), dim3(kBlock), 0, s, a);
+  if (bits == 8)
+    hipLaunchKernelGGL((k_stage1<MODE, 8, U>), dim3(blocks), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_stage1<MODE, 4, U>), dim3(blocks), dim3(kBlock), 0, s, a);
   return launch_status();
 }
 
@@ -136,19 +145,22 @@ constexpr int u_reduce(int mode) {
 }
 
 template <int MODE, int P>
-void launch_reduce_p(const ReduceArgs& a, uint32_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL((k_reduce<MODE, P, u_reduce(MODE)>), dim3(blocks), dim3(kBlock), 0, s, a);
+void launch_reduce_p(const ReduceArgs& a, int bits, uint32_t blocks, hipStream_t s) {
+  if (bits == 8)
+    hipLaunchKernelGGL((k_reduce<MODE, 8, P, u_reduce(MODE)>), dim3(blocks), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_reduce<MODE, 4, P, u_reduce(MODE)>), dim3(blocks), dim3(kBlock), 0, s, a);
 }
 
 template <int MODE>
-int launch_reduce(int P, const ReduceArgs& a, hipStream_t s) {
+int launch_reduce(int P, const ReduceArgs& a, int bits, hipStream_t s) {
   constexpr int U = u_reduce(MODE);
   const uint64_t nslices = ((uint64_t)a.groups + 1) / 2;
   if (nslices == 0) return ECHO_SUCCESS;
   const uint32_t blocks = blocks_for((nslices + U - 1) / U);
   switch (P) {
 #define ECHO_REDUCE_CASE(p) \
-  case p: launch_reduce_p<MODE, p>(a, blocks, s); break;
+  case p: launch_reduce_p<MODE, p>(a, bits, blocks, s); break;
     ECHO_REDUCE_CASE(1) ECHO_REDUCE_CASE(2) ECHO_REDUCE_CASE(3) ECHO_REDUCE_CASE(4)
     ECHO_REDUCE_CASE(5) ECHO_REDUCE_CASE(6) ECHO_REDUCE_CASE(7) ECHO_REDUCE_CASE(8)
     ECHO_REDUCE_CASE(9) ECHO_REDUCE_CASE(10) ECHO_REDUCE_CASE(11) ECHO_REDUCE_CASE(12)
@@ -159,13 +171,16 @@ int launch_reduce(int P, const ReduceArgs& a, hipStream_t s) {
   return launch_status();
 }
 
-int launch_decode(const DecodeArgs& a, uint32_t nseg, hipStream_t s) {
+int launch_decode(const DecodeArgs& a, uint32_t nseg, int bits, hipStream_t s) {
   const uint64_t nquads = ((uint64_t)a.groups + 3) / 4;
   if (nquads == 0 || nseg == 0) return ECHO_SUCCESS;
   uint32_t blocks = blocks_for((nquads + kUD - 1) / kUD);
   const uint32_t cap = kMaxBlocks / nseg > 0 ? kMaxBlocks / nseg : 1;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((k_decode<kUD>), dim3(blocks, nseg), dim3(kBlock), 0, s, a);
+  if (bits == 8)
+    hipLaunchKernelGGL((k_decode<8, kUD>), dim3(blocks, nseg), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_decode<4, kUD>), dim3(blocks, nseg), dim3(kBlock), 0, s, a);
   return launch_status();
 }
 
@@ -202,7 +217,7 @@ void add_remote_inputs(Aliases& al, const echo_state* st, const uint8_t* const* 
                        const float* const* scales, int64_t chunk) {
   for (int q = 0; q < st->nranks; ++q) {
     if (q == st->rank) continue;
-    al.in(codes[q], chunk / 2);
+    al.in(codes[q], code_bytes(chunk, st->bits));
     al.in(scales[q], chunk / ECHO_GROUP * 4);
   }
 }
@@ -220,7 +235,7 @@ int run_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes, floa
   a.groups_work = g.groups - g.chunk_groups;
   a.own_g0 = g.own_g0;
   a.own_g1 = g.own_g1;
-  return launch_stage1<kEntryFused>(a, s);
+  return launch_stage1<kEntryFused>(a, st->bits, s);
 }
 
 int run_reduce_own(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
@@ -243,7 +258,7 @@ int run_reduce_own(const echo_state* st, const uint16_t* x, const uint8_t* const
   a.ms = st->m_slow + e0;
   a.groups = g.chunk_groups;
   a.rank = st->rank;
-  return launch_reduce<kOwnFused>(st->nranks, a, s);
+  return launch_reduce<kOwnFused>(st->nranks, a, st->bits, s);
 }
 
 int run_exit(const echo_state* st, const uint8_t* const* gath_codes,
@@ -260,7 +275,7 @@ int run_exit(const echo_state* st, const uint8_t* const* gath_codes,
     ++k;
   }
   a.groups = g.chunk_groups;
-  return launch_decode(a, k, s);
+  return launch_decode(a, k, st->bits, s);
 }
 
 // ---- the uncompensated call: x' = f32(x), no averages ----------------------
@@ -276,7 +291,7 @@ int run_entry_plain(const echo_state* geo, const uint16_t* x, uint8_t* send_code
   a.groups_work = g.groups - g.chunk_groups;
   a.own_g0 = g.own_g0;
   a.own_g1 = g.own_g1;
-  return launch_stage1<kEntryPlain>(a, s);
+  return launch_stage1<kEntryPlain>(a, geo->bits, s);
 }
 
 int run_reduce_plain(const echo_state* geo, const uint16_t* x, const uint8_t* const* recv_codes,
@@ -296,7 +311,7 @@ int run_reduce_plain(const echo_state* geo, const uint16_t* x, const uint8_t* co
   a.x = x + e0;
   a.groups = g.chunk_groups;
   a.rank = geo->rank;
-  return launch_reduce<kOwnPlain>(geo->nranks, a, s);
+  return launch_reduce<kOwnPlain>(geo->nranks, a, geo->bits, s);
 }
 
 // ---- reduce-scatter only -----------------------------------------------------
@@ -317,7 +332,7 @@ int run_rs_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const*
   a.ms = st->m_slow + e0;
   a.groups = g.chunk_groups;
   a.rank = st->rank;
-  return launch_reduce<kOwnRS>(st->nranks, a, s);
+  return launch_reduce<kOwnRS>(st->nranks, a, st->bits, s);
 }
 
 int check_rs_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
@@ -353,6 +368,8 @@ int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int
   st->n = n;
   st->nranks = nranks;
   st->rank = rank;
+  st->bits = 4;
+  st->reserved = 0;
   const int64_t n4 = n / 4;
   int64_t blocks = (n4 + kBlock - 1) / kBlock;
   if (blocks > (int64_t)kMaxBlocks) blocks = kMaxBlocks;
@@ -369,7 +386,7 @@ int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* 
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return ECHO_ERR_ALIGNMENT;
   const int64_t n = st->n;
   Aliases al;
-  al.out(codes, n / 2);
+  al.out(codes, code_bytes(n, st->bits));
   al.out(scales, n / ECHO_GROUP * 4);
   al.in(x, n * 2);
   al.in(st->m_fast, n * 4);
@@ -384,13 +401,15 @@ int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* 
   a.e2 = nullptr;
   a.groups_work = (uint32_t)(n / ECHO_GROUP);
   a.own_g0 = a.own_g1 = 0;
-  return launch_stage1<kEncode>(a, (hipStream_t)stream);
+  return launch_stage1<kEncode>(a, st->bits, (hipStream_t)stream);
 }
 
-int echo_reduce_shard(int32_t nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
-                      const float* const* shard_scales, uint8_t* out_codes, float* out_scales,
-                      uint16_t* out_y, float* out_e2, echo_stream_t stream) {
+int echo_reduce_shard(int32_t nranks, int64_t chunk_n, int32_t bits,
+                      const uint8_t* const* shard_codes, const float* const* shard_scales,
+                      uint8_t* out_codes, float* out_scales, uint16_t* out_y, float* out_e2,
+                      echo_stream_t stream) {
   if (nranks < 1 || nranks > ECHO_MAX_RANKS) return ECHO_ERR_RANKS;
+  if (!bits_ok(bits)) return ECHO_ERR_FORMAT;
   if (chunk_n <= 0 || chunk_n > ECHO_MAX_ELEMENTS || chunk_n % ECHO_GROUP != 0) return ECHO_ERR_SHAPE;
   if (!shard_codes || !shard_scales || !out_codes || !out_scales) return ECHO_ERR_INVALID_ARGUMENT;
   for (int q = 0; q < nranks; ++q) {
@@ -401,12 +420,12 @@ int echo_reduce_shard(int32_t nranks, int64_t chunk_n, const uint8_t* const* sha
       !aligned(out_e2, 16))
     return ECHO_ERR_ALIGNMENT;
   Aliases al;
-  al.out(out_codes, chunk_n / 2);
+  al.out(out_codes, code_bytes(chunk_n, bits));
   al.out(out_scales, chunk_n / ECHO_GROUP * 4);
   al.out(out_y, chunk_n * 2);
   al.out(out_e2, chunk_n * 4);
   for (int q = 0; q < nranks; ++q) {
-    al.in(shard_codes[q], chunk_n / 2);
+    al.in(shard_codes[q], code_bytes(chunk_n, bits));
     al.in(shard_scales[q], chunk_n / ECHO_GROUP * 4);
   }
   if (!al.ok()) return ECHO_ERR_ALIAS;
@@ -422,17 +441,18 @@ int echo_reduce_shard(int32_t nranks, int64_t chunk_n, const uint8_t* const* sha
   a.e2 = out_e2;
   a.groups = (uint32_t)(chunk_n / ECHO_GROUP);
   a.rank = -1;
-  return launch_reduce<kShard>(nranks, a, (hipStream_t)stream);
+  return launch_reduce<kShard>(nranks, a, bits, (hipStream_t)stream);
 }
 
-int echo_decode(int64_t n, const uint8_t* codes, const float* scales, uint16_t* y,
+int echo_decode(int64_t n, int32_t bits, const uint8_t* codes, const float* scales, uint16_t* y,
                 echo_stream_t stream) {
   if (n <= 0 || n > ECHO_MAX_ELEMENTS || n % ECHO_GROUP != 0) return ECHO_ERR_SHAPE;
+  if (!bits_ok(bits)) return ECHO_ERR_FORMAT;
   if (!codes || !scales || !y) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(y, 16)) return ECHO_ERR_ALIGNMENT;
   Aliases al;
   al.out(y, n * 2);
-  al.in(codes, n / 2);
+  al.in(codes, code_bytes(n, bits));
   al.in(scales, n / ECHO_GROUP * 4);
   if (!al.ok()) return ECHO_ERR_ALIAS;
   DecodeArgs a;
@@ -441,7 +461,7 @@ int echo_decode(int64_t n, const uint8_t* codes, const float* scales, uint16_t* 
   a.seg[0].scales = scales;
   a.seg[0].y = y;
   a.groups = (uint32_t)(n / ECHO_GROUP);
-  return launch_decode(a, 1, (hipStream_t)stream);
+  return launch_decode(a, 1, bits, (hipStream_t)stream);
 }
 
 int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
@@ -456,7 +476,7 @@ int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
   al.out(st->m_fast, g.n * 4);
   al.out(st->m_slow, g.n * 4);
   al.in(x, g.n * 2);
-  al.in(codes1, g.n / 2);
+  al.in(codes1, code_bytes(g.n, st->bits));
   al.in(scales1, g.n / ECHO_GROUP * 4);
   al.in(e2_own, g.chunk * 4);
   if (!al.ok()) return ECHO_ERR_ALIAS;
@@ -470,7 +490,7 @@ int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
   a.groups_work = g.groups;
   a.own_g0 = g.own_g0;
   a.own_g1 = g.own_g1;
-  return launch_stage1<kUpdate>(a, (hipStream_t)stream);
+  return launch_stage1<kUpdate>(a, st->bits, (hipStream_t)stream);
 }
 
 int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes,
@@ -482,7 +502,7 @@ int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes
     return ECHO_ERR_ALIGNMENT;
   const int64_t n = st->n;
   Aliases al;
-  al.out(send_codes, n / 2);
+  al.out(send_codes, code_bytes(n, st->bits));
   al.out(send_scales, n / ECHO_GROUP * 4);
   al.out(st->m_fast, n * 4);
   al.out(st->m_slow, n * 4);
@@ -503,7 +523,7 @@ int echo_call_reduce(const echo_state* st, const uint16_t* x, const uint8_t* con
   if (rc) return rc;
   const Geometry g = geometry(st);
   Aliases al;
-  al.out(own_codes2, g.chunk / 2);
+  al.out(own_codes2, code_bytes(g.chunk, st->bits));
   al.out(own_scales2, g.chunk / ECHO_GROUP * 4);
   al.out(y, g.n * 2);
   al.out(st->m_fast, g.n * 4);
@@ -551,9 +571,9 @@ int echo_call(const echo_state* st, const uint16_t* x, const uint8_t* const* rec
   if (rc) return rc;
   const Geometry g = geometry(st);
   Aliases al;
-  al.out(send_codes, g.n / 2);
+  al.out(send_codes, code_bytes(g.n, st->bits));
   al.out(send_scales, g.n / ECHO_GROUP * 4);
-  al.out(own_codes2, g.chunk / 2);
+  al.out(own_codes2, code_bytes(g.chunk, st->bits));
   al.out(own_scales2, g.chunk / ECHO_GROUP * 4);
   al.out(y, g.n * 2);
   al.out(st->m_fast, g.n * 4);
@@ -571,7 +591,7 @@ int echo_call(const echo_state* st, const uint16_t* x, const uint8_t* const* rec
   return run_exit(st, gath_codes, gath_scales, y, s);
 }
 
-int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
+int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, int32_t bits, const uint16_t* x,
                     const uint8_t* const* recv_codes, const float* const* recv_scales,
                     const uint8_t* const* gath_codes, const float* const* gath_scales,
                     uint8_t* send_codes, float* send_scales, uint8_t* own_codes2,
@@ -579,6 +599,7 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
   int rc = check_ranks_shape(n, nranks);
   if (rc) return rc;
   if (rank < 0 || rank >= nranks) return ECHO_ERR_RANKS;
+  if (!bits_ok(bits)) return ECHO_ERR_FORMAT;
   if (!x || !send_codes || !send_scales || !own_codes2 || !own_scales2 || !y)
     return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(send_codes, 16) || !aligned(send_scales, 4) ||
@@ -591,15 +612,17 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
   geo.n = n;
   geo.nranks = nranks;
   geo.rank = rank;
+  geo.bits = bits;
+  geo.reserved = 0;
   rc = check_remote_arrays(&geo, recv_codes, recv_scales);
   if (rc) return rc;
   rc = check_remote_arrays(&geo, gath_codes, gath_scales);
   if (rc) return rc;
   const Geometry g = geometry(&geo);
   Aliases al;
-  al.out(send_codes, g.n / 2);
+  al.out(send_codes, code_bytes(g.n, bits));
   al.out(send_scales, g.n / ECHO_GROUP * 4);
-  al.out(own_codes2, g.chunk / 2);
+  al.out(own_codes2, code_bytes(g.chunk, bits));
   al.out(own_scales2, g.chunk / ECHO_GROUP * 4);
   al.out(y, g.n * 2);
   al.in(x, g.n * 2);
@@ -615,10 +638,11 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
   return run_exit(&geo, gath_codes, gath_scales, y, s);
 }
 
-int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
-                          const float* const* shard_scales, uint16_t* out_y, float* out_e2,
-                          echo_stream_t stream) {
+int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, int32_t bits,
+                          const uint8_t* const* shard_codes, const float* const* shard_scales,
+                          uint16_t* out_y, float* out_e2, echo_stream_t stream) {
   if (nranks < 1 || nranks > ECHO_MAX_RANKS) return ECHO_ERR_RANKS;
+  if (!bits_ok(bits)) return ECHO_ERR_FORMAT;
   if (chunk_n <= 0 || chunk_n > ECHO_MAX_ELEMENTS || chunk_n % ECHO_GROUP != 0) return ECHO_ERR_SHAPE;
   if (!shard_codes || !shard_scales || !out_y) return ECHO_ERR_INVALID_ARGUMENT;
   for (int q = 0; q < nranks; ++q) {
@@ -630,7 +654,7 @@ int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, const uint8_t* const*
   al.out(out_y, chunk_n * 2);
   al.out(out_e2, chunk_n * 4);
   for (int q = 0; q < nranks; ++q) {
-    al.in(shard_codes[q], chunk_n / 2);
+    al.in(shard_codes[q], code_bytes(chunk_n, bits));
     al.in(shard_scales[q], chunk_n / ECHO_GROUP * 4);
   }
   if (!al.ok()) return ECHO_ERR_ALIAS;
@@ -644,7 +668,7 @@ int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, const uint8_t* const*
   a.e2 = out_e2;
   a.groups = (uint32_t)(chunk_n / ECHO_GROUP);
   a.rank = -1;
-  return launch_reduce<kShardSum>(nranks, a, (hipStream_t)stream);
+  return launch_reduce<kShardSum>(nranks, a, bits, (hipStream_t)stream);
 }
 
 int echo_rs_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
@@ -671,7 +695,7 @@ int echo_rs_call(const echo_state* st, const uint16_t* x, const uint8_t* const* 
   rc = check_rs_reduce(st, x, recv_codes, recv_scales, y_own, al);
   if (rc) return rc;
   const int64_t n = st->n;
-  al.out(send_codes, n / 2);
+  al.out(send_codes, code_bytes(n, st->bits));
   al.out(send_scales, n / ECHO_GROUP * 4);
   al.out(st->m_fast, n * 4);
   al.out(st->m_slow, n * 4);
@@ -687,6 +711,7 @@ int echo_get_config(echo_config* out) {
   out->abi_version = ECHO_ABI_VERSION;
   out->group = ECHO_GROUP;
   out->qmax = ECHO_QMAX;
+  out->qmax8 = ECHO_QMAX8;
   out->max_ranks = ECHO_MAX_RANKS;
   out->w_fast = ECHO_W_FAST;
   out->w_slow = ECHO_W_SLOW;
@@ -707,6 +732,7 @@ const char* echo_status_string(int status) {
     case ECHO_ERR_RANKS: return "bad rank count or rank index";
     case ECHO_ERR_HIP: return "HIP runtime error";
     case ECHO_ERR_ALIAS: return "outputs overlap each other or an input";
+    case ECHO_ERR_FORMAT: return "code width must be 4 or 8 bits";
     default: return "unknown status";
   }
 }

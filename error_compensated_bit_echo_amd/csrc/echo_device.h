@@ -28,7 +28,10 @@
 namespace echo {
 
 constexpr int kGroup = ECHO_GROUP;
-constexpr float kQmax = (float)ECHO_QMAX;
+// code widths: 4 -> packed nibbles, codes in [-7, 7]; 8 -> one two's-
+// complement byte per element, codes in [-127, 127] (the 8-bit promotion)
+template <int BITS>
+__host__ __device__ constexpr float qmax_of() { return BITS == 8 ? (float)ECHO_QMAX8 : (float)ECHO_QMAX; }
 constexpr int kMaxRanks = ECHO_MAX_RANKS;
 constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
 
@@ -134,8 +137,9 @@ __device__ __forceinline__ float corrected(float xf, float mf, float ms) {
 }
 
 // The group scale from the group's absmax: s = amax / 7 (IEEE division).
+template <int BITS>
 __device__ __forceinline__ float scale_of(uint32_t amax_bits) {
-  return __uint_as_float(amax_bits) / kQmax;
+  return __uint_as_float(amax_bits) / qmax_of<BITS>();
 }
 
 // Divisor used for the codes: s itself, or 1 when s == 0.  s == 0 means
@@ -147,9 +151,10 @@ __device__ __forceinline__ float code_divisor(float s) { return s == 0.0f ? 1.0f
 // (A reciprocal-multiply with an exact fallback near half-integers gives the
 // same codes but measured no faster on MI355X: these kernels are not bound
 // by the division.)
+template <int BITS>
 __device__ __forceinline__ int quant_code(float v, float sdiv) {
   float t = __builtin_rintf(v / sdiv);
-  t = fminf(fmaxf(t, -kQmax), kQmax);
+  t = fminf(fmaxf(t, -qmax_of<BITS>()), qmax_of<BITS>());
   return (int)t;
 }
 
@@ -162,6 +167,38 @@ __device__ __forceinline__ uint32_t pack_nib4(const int (&q)[4]) {
 // nibble k of a packed word -> signed code (sign-extend the 4-bit field)
 __device__ __forceinline__ int nib(uint32_t w, int k) {
   return (int)(w << (28 - 4 * k)) >> 28;
+}
+
+// code k of a packed word of BITS-wide codes (sign-extended)
+template <int BITS>
+__device__ __forceinline__ int code_at(uint32_t w, int k) {
+  if (BITS == 8) return (int)(w << (24 - 8 * k)) >> 24;
+  return nib(w, k);
+}
+
+// 4 codes -> one word (16 bits of nibbles, or 32 bits of bytes)
+template <int BITS>
+__device__ __forceinline__ uint32_t pack_codes4(const int (&q)[4]) {
+  if (BITS == 8)
+    return ((uint32_t)q[0] & 0xFFu) | (((uint32_t)q[1] & 0xFFu) << 8) |
+           (((uint32_t)q[2] & 0xFFu) << 16) | (((uint32_t)q[3] & 0xFFu) << 24);
+  return pack_nib4(q);
+}
+
+// byte offset of element e's code, and the 4 codes a lane holds
+template <int BITS>
+__device__ __forceinline__ int64_t code_byte(int64_t e) { return BITS == 8 ? e : e / 2; }
+
+template <int BITS>
+__device__ __forceinline__ uint32_t load_codes4(const uint8_t* codes, int64_t e) {
+  if (BITS == 8) return *reinterpret_cast<const uint32_t*>(codes + e);
+  return *reinterpret_cast<const uint16_t*>(codes + e / 2);
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_codes4(uint8_t* codes, int64_t e, uint32_t w) {
+  if (BITS == 8) st_stream(reinterpret_cast<uint32_t*>(codes + e), w);
+  else st_stream(reinterpret_cast<uint16_t*>(codes + e / 2), (uint16_t)w);
 }
 
 // m <- (B*m) + (A*r) for both averages
@@ -192,7 +229,7 @@ struct Stage1Args {
   uint32_t own_g1;
 };
 
-template <int MODE, int U>
+template <int MODE, int BITS, int U>
 __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
   const int lane = threadIdx.x & 63;
   const uint32_t half = (uint32_t)lane >> 5;
@@ -234,7 +271,7 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
           s = make_float4(sv.x, sv.y, sv.z, sv.w);
         }
         if (MODE == kUpdate) {
-          cw[u] = *reinterpret_cast<const uint16_t*>(a.codes + e / 2);
+          cw[u] = load_codes4<BITS>(a.codes, e);
           sc[u] = a.scales[g[u]];
           if (own[u]) {
             float4 t = *reinterpret_cast<const float4*>(a.e2 + (e - (int64_t)a.own_g0 * kGroup));
@@ -257,18 +294,18 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
       float d1[4];
       if (MODE == kUpdate) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) d1[k] = (float)nib(cw[u], k) * sc[u];
+        for (int k = 0; k < 4; ++k) d1[k] = (float)code_at<BITS>(cw[u], k) * sc[u];
       } else {
         uint32_t m = max(max(abs_bits(xp[0]), abs_bits(xp[1])), max(abs_bits(xp[2]), abs_bits(xp[3])));
         m = halfwave_max(m);
-        const float s = scale_of(m);
+        const float s = scale_of<BITS>(m);
         const float sd = code_divisor(s);
         int q[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) q[k] = quant_code(xp[k], sd);
+        for (int k = 0; k < 4; ++k) q[k] = quant_code<BITS>(xp[k], sd);
         const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
         if (ok[u]) {
-          st_stream(reinterpret_cast<uint16_t*>(a.codes + e / 2), (uint16_t)pack_nib4(q));
+          store_codes4<BITS>(a.codes, e, pack_codes4<BITS>(q));
           if (sub == 0) a.scales[g[u]] = s;
         }
 #pragma unroll
@@ -319,7 +356,7 @@ struct ReduceArgs {
   int32_t rank;                      // own modes: the slot computed in registers
 };
 
-template <int MODE, int P, int U>
+template <int MODE, int BITS, int P, int U>
 __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
   const int lane = threadIdx.x & 63;
   const uint32_t half = (uint32_t)lane >> 5;
@@ -346,7 +383,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
         cw[u][q] = 0u;
         sc[u][q] = 0.f;
         if (ok[u] && !(own_in_registers(MODE) && q == a.rank)) {
-          cw[u][q] = *reinterpret_cast<const uint16_t*>(a.codes[q] + e / 2);
+          cw[u][q] = load_codes4<BITS>(a.codes[q], e);
           sc[u][q] = a.scales[q][g[u]];
         }
       }
@@ -378,10 +415,10 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
           xp[k] = own_reads_state(MODE) ? corrected(xf[u][k], mf[u][k], ms[u][k]) : xf[u][k];
         uint32_t m = max(max(abs_bits(xp[0]), abs_bits(xp[1])), max(abs_bits(xp[2]), abs_bits(xp[3])));
         m = halfwave_max(m);
-        const float s1 = scale_of(m);
+        const float s1 = scale_of<BITS>(m);
         const float sd = code_divisor(s1);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) d_own[k] = (float)quant_code(xp[k], sd) * s1;
+        for (int k = 0; k < 4; ++k) d_own[k] = (float)quant_code<BITS>(xp[k], sd) * s1;
       }
 
       // S = d_0 + d_1 + ... + d_{P-1}, in rank order
@@ -392,7 +429,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
         for (int k = 0; k < 4; ++k) {
           float d;
           if (own_in_registers(MODE) && q == a.rank) d = d_own[k];
-          else d = (float)nib(cw[u][q], k) * sc[u][q];
+          else d = (float)code_at<BITS>(cw[u][q], k) * sc[u][q];
           S[k] = (q == 0) ? d : S[k] + d;
         }
       }
@@ -405,10 +442,10 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       if (requantizes(MODE)) {
         uint32_t m2 = max(max(abs_bits(S[0]), abs_bits(S[1])), max(abs_bits(S[2]), abs_bits(S[3])));
         m2 = halfwave_max(m2);
-        s2 = scale_of(m2);
+        s2 = scale_of<BITS>(m2);
         const float sd2 = code_divisor(s2);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) q2[k] = quant_code(S[k], sd2);
+        for (int k = 0; k < 4; ++k) q2[k] = quant_code<BITS>(S[k], sd2);
         y01 = pack_bf16x2((float)q2[0] * s2, (float)q2[1] * s2);
         y23 = pack_bf16x2((float)q2[2] * s2, (float)q2[3] * s2);
       } else {
@@ -423,7 +460,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
 
       if (ok[u]) {
         if (requantizes(MODE)) {
-          st_stream(reinterpret_cast<uint16_t*>(a.out_codes + e / 2), (uint16_t)pack_nib4(q2));
+          store_codes4<BITS>(a.out_codes, e, pack_codes4<BITS>(q2));
           if (sub == 0) a.out_scales[g[u]] = s2;
         }
         if (a.y) st_stream(reinterpret_cast<u32x2*>(a.y + e), u32x2{y01, y23});
@@ -449,7 +486,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
 // exit kernel: y = bf16(code * scale); blockIdx.y selects a segment
 
 struct DecodeSeg {
-  const uint8_t* codes;  // [groups*64]
+  const uint8_t* codes;  // [groups*128*BITS/8]
   const float* scales;   // [groups]
   uint16_t* y;           // [groups*128]
 };
@@ -459,7 +496,7 @@ struct DecodeArgs {
   uint32_t groups;  // groups per segment
 };
 
-template <int U>
+template <int BITS, int U>
 __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const uint32_t row = (uint32_t)lane >> 4;  // group within the wave's quad of groups
@@ -471,7 +508,7 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
   const DecodeSeg sg = a.seg[blockIdx.y];
 
   for (uint32_t t0 = wave * U; t0 < nquads; t0 += nwaves * U) {
-    uint32_t cw[U];
+    uint32_t cw[U][2];  // 8 codes: one word of nibbles, or two words of bytes
     float sc[U];
     bool ok[U];
     uint32_t g[U];
@@ -480,20 +517,31 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
       const uint32_t v = 4u * (t0 + u) + row;
       ok[u] = (t0 + u < nquads) && (v < a.groups);
       g[u] = ok[u] ? v : 0u;
-      cw[u] = 0u;
+      cw[u][0] = cw[u][1] = 0u;
       sc[u] = 0.f;
       if (ok[u]) {
-        cw[u] = *reinterpret_cast<const uint32_t*>(sg.codes + (int64_t)g[u] * (kGroup / 2) + sub * 4);
+        const int64_t e = (int64_t)g[u] * kGroup + sub * 8;
+        if (BITS == 8) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(sg.codes + e);
+          cw[u][0] = w.x;
+          cw[u][1] = w.y;
+        } else {
+          cw[u][0] = *reinterpret_cast<const uint32_t*>(sg.codes + e / 2);
+        }
         sc[u] = sg.scales[g[u]];
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      int c[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        c[k] = BITS == 8 ? code_at<8>(cw[u][k / 4], k % 4) : nib(cw[u][0], k);
       uint4 o;
-      o.x = pack_bf16x2((float)nib(cw[u], 0) * sc[u], (float)nib(cw[u], 1) * sc[u]);
-      o.y = pack_bf16x2((float)nib(cw[u], 2) * sc[u], (float)nib(cw[u], 3) * sc[u]);
-      o.z = pack_bf16x2((float)nib(cw[u], 4) * sc[u], (float)nib(cw[u], 5) * sc[u]);
-      o.w = pack_bf16x2((float)nib(cw[u], 6) * sc[u], (float)nib(cw[u], 7) * sc[u]);
+      o.x = pack_bf16x2((float)c[0] * sc[u], (float)c[1] * sc[u]);
+      o.y = pack_bf16x2((float)c[2] * sc[u], (float)c[3] * sc[u]);
+      o.z = pack_bf16x2((float)c[4] * sc[u], (float)c[5] * sc[u]);
+      o.w = pack_bf16x2((float)c[6] * sc[u], (float)c[7] * sc[u]);
       if (ok[u])
         st_stream(reinterpret_cast<u32x4*>(sg.y + (int64_t)g[u] * kGroup + sub * 8), u32x4{o.x, o.y, o.z, o.w});
     }

@@ -181,23 +181,30 @@ def _valid_code_bytes() -> np.ndarray:
 
 def int4_message(n: int, key: int, scale_lo: float = 0.05, scale_hi: float = 0.55,
                  zero_group_frac: float = 0.0, any_byte: bool = False,
-                 group: int = 128):
-    """A seeded packed-int4 message for n elements: (codes u8[n/2], scales f32[n/group]).
-    Bytes are drawn uniformly from the 225 bytes without a -8 field (or from
-    all 256 when any_byte); scales uniformly from [scale_lo, scale_hi); a
-    seeded fraction of groups is all-zero (codes 0, scale 0)."""
-    alphabet = np.arange(256, dtype=np.uint8) if any_byte else _valid_code_bytes()
+                 group: int = 128, bits: int = 4):
+    """A seeded message of n codes: (codes u8[n/2] for 4-bit or u8[n] for 8-bit
+    codes, scales f32[n/group]).  4-bit: bytes drawn uniformly from the 225
+    bytes without a -8 field; 8-bit: from the 255 bytes other than 0x80 (-128);
+    all 256 when any_byte.  Scales uniform in [scale_lo, scale_hi); a seeded
+    fraction of groups is all-zero (codes 0, scale 0)."""
+    if any_byte:
+        alphabet = np.arange(256, dtype=np.uint8)
+    elif bits == 8:
+        alphabet = np.array([b for b in range(256) if b != 0x80], dtype=np.uint8)
+    else:
+        alphabet = _valid_code_bytes()
     ckey = stream_key(key, "codes")
+    nbytes = n if bits == 8 else n // 2
 
     def fill(lo, hi, out):
         out[:] = alphabet[(_bits(ckey, lo, hi) % np.uint64(alphabet.size)).astype(np.int64)]
-    codes = _chunked(n // 2, fill, np.uint8)
+    codes = _chunked(nbytes, fill, np.uint8)
     g = n // group
     scales = (scale_lo + (scale_hi - scale_lo) * uniform(g, stream_key(key, "scales"))).astype(np.float32)
     if zero_group_frac > 0.0:
         zg = uniform(g, stream_key(key, "zero")) < zero_group_frac
         scales[zg] = 0.0
-        cv = codes.reshape(g, group // 2)
+        cv = codes.reshape(g, nbytes // g)
         cv[zg] = 0
     return codes, scales
 

@@ -29,6 +29,15 @@
  *   int4 codes    uint8_t[n/2]; byte k holds element 2k in bits 0..3 and
  *                 element 2k+1 in bits 4..7, two's complement; the encoder
  *                 emits codes in [-7, 7] only (a 0x8 field decodes as -8).
+ *   int8 codes    uint8_t[n]: one two's-complement byte per element, codes in
+ *                 [-127, 127] (0x80 decodes as -128); used when a call is
+ *                 promoted to 8 bits.  The pages promote the first half of the
+ *                 layers to 8 bits in serving ("Tensor-parallel traffic drops
+ *                 to 4 bits", Perspective).  The width is st->bits for calls
+ *                 that take a state (set it before each call; the averages do
+ *                 not depend on it) and the `bits` argument otherwise; every
+ *                 "codes" array below then has n/2 (4-bit) or n (8-bit)
+ *                 bytes, and QMAX is 7 or 127.
  *   scales        float[n/128]; group g covers elements [128g, 128g+128);
  *                 element value = code * scale.  Scale 0 means all codes 0.
  *   averages      float[n] each (m_fast, m_slow), caller-owned.
@@ -68,6 +77,7 @@ extern "C" {
 /* ---- named parameters (readings of what the pages leave open) ------------ */
 #define ECHO_GROUP 128          /* elements per scale */
 #define ECHO_QMAX 7             /* symmetric int4 range [-7, 7] */
+#define ECHO_QMAX8 127          /* 8-bit codes (a promoted call): [-127, 127] */
 #define ECHO_W_FAST 0.5f        /* correction = W_FAST*m_fast + W_SLOW*m_slow */
 #define ECHO_W_SLOW 0.5f
 #define ECHO_BETA_FAST 0.5f     /* m_fast <- BETA_FAST*m_fast + ALPHA_FAST*r */
@@ -76,7 +86,7 @@ extern "C" {
 #define ECHO_ALPHA_SLOW 0.125f
 #define ECHO_MAX_RANKS 16
 #define ECHO_MAX_ELEMENTS (INT64_C(1) << 37)
-#define ECHO_ABI_VERSION 1
+#define ECHO_ABI_VERSION 2
 
 /* ---- status codes --------------------------------------------------------- */
 #define ECHO_SUCCESS 0
@@ -86,6 +96,7 @@ extern "C" {
 #define ECHO_ERR_RANKS -4            /* P or rank out of range */
 #define ECHO_ERR_HIP -5              /* the HIP runtime reported an error */
 #define ECHO_ERR_ALIAS -6            /* outputs overlap each other or an input */
+#define ECHO_ERR_FORMAT -7           /* code width other than 4 or 8 bits */
 
 typedef void* echo_stream_t; /* a hipStream_t */
 
@@ -99,16 +110,18 @@ typedef struct echo_state {
   int64_t n;     /* elements of this rank's tensor */
   int32_t nranks;
   int32_t rank;
+  int32_t bits;     /* code width of this call's messages: 4 (default) or 8 */
+  int32_t reserved; /* 0 */
 } echo_state;
 
 typedef struct echo_config {
-  int32_t abi_version, group, qmax, max_ranks;
+  int32_t abi_version, group, qmax, qmax8, max_ranks;
   float w_fast, w_slow, beta_fast, alpha_fast, beta_slow, alpha_slow;
   int64_t max_elements;
 } echo_config;
 
-/* Fill *st and enqueue zero-fills of m_fast and m_slow (the averages start at
- * zero).  Validates shape, ranks and alignment. */
+/* Fill *st (bits = 4) and enqueue zero-fills of m_fast and m_slow (the
+ * averages start at zero).  Validates shape, ranks and alignment. */
 int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int32_t nranks,
                     int32_t rank, echo_stream_t stream);
 
@@ -132,13 +145,14 @@ int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* 
  * [chunk_n/128].  Optional outputs (NULL to skip): out_y[chunk_n] =
  * bf16(code2*s2) rounded to nearest even, out_e2[chunk_n] = f32(y) - S.
  * chunk_n > 0 and chunk_n % 128 == 0. */
-int echo_reduce_shard(int32_t nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
-                      const float* const* shard_scales, uint8_t* out_codes, float* out_scales,
-                      uint16_t* out_y, float* out_e2, echo_stream_t stream);
+int echo_reduce_shard(int32_t nranks, int64_t chunk_n, int32_t bits,
+                      const uint8_t* const* shard_codes, const float* const* shard_scales,
+                      uint8_t* out_codes, float* out_scales, uint16_t* out_y, float* out_e2,
+                      echo_stream_t stream);
 
 /* Exit pass over n elements: y = bf16(code*scale), round to nearest even.
  * n > 0 and n % 128 == 0. */
-int echo_decode(int64_t n, const uint8_t* codes, const float* scales, uint16_t* y,
+int echo_decode(int64_t n, int32_t bits, const uint8_t* codes, const float* scales, uint16_t* y,
                 echo_stream_t stream);
 
 /* Update ("Tensor-parallel traffic drops to 4 bits", Interpretation: the
@@ -195,7 +209,7 @@ int echo_call(const echo_state* st, const uint16_t* x, const uint8_t* const* rec
  * echo_call, with the rank geometry given directly.  Also the control of the
  * deep-chain experiment, and the critical path the compensation is measured
  * against. */
-int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
+int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, int32_t bits, const uint16_t* x,
                     const uint8_t* const* recv_codes, const float* const* recv_scales,
                     const uint8_t* const* gath_codes, const float* const* gath_scales,
                     uint8_t* send_codes, float* send_scales, uint8_t* own_codes2,
@@ -221,9 +235,9 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, const uint16_t* x,
 
 /* Rank-order sum of P stage-1 shards output as bf16: out_y[chunk_n] =
  * bf16(S); out_e2 (nullable) = f32(out_y) - S.  Unfused. */
-int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, const uint8_t* const* shard_codes,
-                          const float* const* shard_scales, uint16_t* out_y, float* out_e2,
-                          echo_stream_t stream);
+int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, int32_t bits,
+                          const uint8_t* const* shard_codes, const float* const* shard_scales,
+                          uint16_t* out_y, float* out_e2, echo_stream_t stream);
 
 /* Reduce phase of the reduce-scatter: the own chunk's correction and stage-1
  * quantization in registers, the rank-order sum with the P-1 incoming shards

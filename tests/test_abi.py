@@ -40,7 +40,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_config_matches_oracle_constants():
     cfg = B.echo_get_config()
-    assert cfg["abi_version"] == B.echo_version() == 1
+    assert cfg["abi_version"] == B.echo_version() == 2
+    assert cfg["qmax8"] == orc.QMAX8 == 127
     assert cfg["group"] == orc.GROUP == 128
     assert cfg["qmax"] == orc.QMAX
     assert cfg["max_ranks"] == orc.MAX_RANKS
@@ -54,7 +55,7 @@ def test_config_matches_oracle_constants():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert B.status_string(code) and B.status_string(code) != "unknown status"
     assert B.status_string(-99) == "unknown status"
 
@@ -68,9 +69,9 @@ def st(n=1024, P=2, rank=0, mf=A, ms=2 * A):
     return B.EchoState(mf, ms, n, P, rank)
 
 
-def rc(fn, *args):
+def rc(fn, *args, **kw):
     with pytest.raises(B.EchoError) as e:
-        fn(*args, stream=0)  # an explicit null stream: no GPU is touched
+        fn(*args, stream=0, **kw)  # an explicit null stream: no GPU is touched
     return e.value.status
 
 
@@ -178,3 +179,16 @@ def test_reduce_scatter_rejections():
     assert rc(B.echo_rs_reduce, s4, 3 * A, recv_c, recv_s, 3 * A + 4096) == -6  # y_own inside x
     assert rc(B.echo_rs_call, s4, 3 * A, recv_c, recv_s, 50 * A, 51 * A, 52 * A + 2) == -3
     assert rc(B.echo_rs_call, s4, 3 * A, recv_c, recv_s, 50 * A, 51 * A, A) == -6  # y_own over m_fast
+
+
+def test_code_width_rejections():
+    s8 = st()
+    s8.bits = 5
+    assert rc(B.echo_encode, s8, 3 * A, 4 * A, 5 * A) == -7
+    assert rc(B.echo_decode, 3 * A, 4 * A, 5 * A, 128, bits=6) == -7
+    assert rc(B.echo_reduce_shard, [3 * A], [5 * A], 7 * A, 8 * A, None, None, 256, bits=2) == -7
+    assert rc(B.echo_reduce_shard_sum, [3 * A], [5 * A], 7 * A, None, 256, bits=16) == -7
+    # 8-bit codes take n bytes: codes ending 496 bytes before x in 4-bit form
+    # (n/2 = 512 bytes from x - 1008) reach 16 bytes into x in 8-bit form
+    s8.bits = 8
+    assert rc(B.echo_encode, s8, 3 * A, 3 * A - 1008, 5 * A) == -6

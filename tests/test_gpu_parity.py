@@ -52,18 +52,23 @@ def state_of(n, seed, scale=0.05):
 SHAPES = [(1, 1), (1, 7), (2, 3), (3, 5), (4, 1), (8, 33), (8, 257), (16, 3), (5, 2049)]
 
 
+def cb(n, bits):
+    return n if bits == 8 else n // 2
+
+
 @pytest.mark.parametrize("P,k", SHAPES)
 @pytest.mark.parametrize("warm", [False, True])
-def test_encode(P, k, warm):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_encode(P, k, warm, bits):
     g = gu()
     n = P * 128 * k
     x = x_of(n, 1000 * P + k)
     mf, ms = state_of(n, k) if warm else (np.zeros(n, np.float32), np.zeros(n, np.float32))
     mfd, msd = g.dev(mf), g.dev(ms)
-    st = B.EchoState(mfd, msd, n, P, P - 1)
-    codes, scales = g.empty_u8(n // 2, 0xAB), g.empty_f32(n // 128, -1.0)
+    st = B.EchoState(mfd, msd, n, P, P - 1, bits=bits)
+    codes, scales = g.empty_u8(cb(n, bits), 0xAB), g.empty_f32(n // 128, -1.0)
     B.echo_encode(st, g.dev(x), codes, scales)
-    want_c, want_s = orc.encode(x, mf, ms)
+    want_c, want_s = orc.encode(x, mf, ms, bits=bits)
     eq(g.host(codes, np.uint8), want_c, "codes")
     eq(g.host(scales, np.float32), want_s, "scales")
     eq(g.host(mfd, np.float32), mf, "m_fast untouched")
@@ -73,80 +78,84 @@ def test_encode(P, k, warm):
 @pytest.mark.parametrize("P", [1, 2, 3, 7, 8, 16])
 @pytest.mark.parametrize("k", [1, 6, 129])
 @pytest.mark.parametrize("any_byte", [False, True])
-def test_reduce_shard(P, k, any_byte):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_reduce_shard(P, k, any_byte, bits):
     g = gu()
     cn = 128 * k
-    msgs = [I.int4_message(cn, I.stream_key("rs", P, k, q), zero_group_frac=0.05, any_byte=any_byte)
-            for q in range(P)]
-    out_c, out_s = g.empty_u8(cn // 2), g.empty_f32(cn // 128)
+    msgs = [I.int4_message(cn, I.stream_key("rs", P, k, q), zero_group_frac=0.05, any_byte=any_byte,
+                           bits=bits) for q in range(P)]
+    out_c, out_s = g.empty_u8(cb(cn, bits)), g.empty_f32(cn // 128)
     out_y, out_e2 = g.empty_bf16(cn), g.empty_f32(cn)
     B.echo_reduce_shard([g.dev(c) for c, _ in msgs], [g.dev(s) for _, s in msgs], out_c, out_s,
-                        out_y, out_e2, chunk_n=cn)
-    wc, ws, wy, we = orc.reduce_chunk([c for c, _ in msgs], [s for _, s in msgs], cn)
+                        out_y, out_e2, chunk_n=cn, bits=bits)
+    wc, ws, wy, we = orc.reduce_chunk([c for c, _ in msgs], [s for _, s in msgs], cn, bits=bits)
     eq(g.host(out_c, np.uint8), wc, "codes2")
     eq(g.host(out_s, np.float32), ws, "scales2")
     eq(g.host(out_y, np.uint16), wy, "y")
     eq(g.host(out_e2, np.float32), we, "e2")
     # optional outputs may be skipped
-    c2, s2 = g.empty_u8(cn // 2), g.empty_f32(cn // 128)
-    B.echo_reduce_shard([g.dev(c) for c, _ in msgs], [g.dev(s) for _, s in msgs], c2, s2, chunk_n=cn)
+    c2, s2 = g.empty_u8(cb(cn, bits)), g.empty_f32(cn // 128)
+    B.echo_reduce_shard([g.dev(c) for c, _ in msgs], [g.dev(s) for _, s in msgs], c2, s2, chunk_n=cn,
+                        bits=bits)
     eq(g.host(c2, np.uint8), wc, "codes2 without y/e2")
 
 
 @pytest.mark.parametrize("k", [1, 3, 4, 5, 1023, 4099])
-def test_decode(k):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_decode(k, bits):
     g = gu()
     n = 128 * k
-    c, s = I.int4_message(n, I.stream_key("dec", k), zero_group_frac=0.1, any_byte=True)
+    c, s = I.int4_message(n, I.stream_key("dec", k), zero_group_frac=0.1, any_byte=True, bits=bits)
     y = g.empty_bf16(n)
-    B.echo_decode(g.dev(c), g.dev(s), y)
-    eq(g.host(y, np.uint16), orc.decode(c, s, n), "y")
+    B.echo_decode(g.dev(c), g.dev(s), y, bits=bits)
+    eq(g.host(y, np.uint16), orc.decode(c, s, n, bits=bits), "y")
 
 
 @pytest.mark.parametrize("P,k", SHAPES)
-def test_update(P, k):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_update(P, k, bits):
     g = gu()
     n = P * 128 * k
     rank = (k * 7) % P
     x = x_of(n, 7 * k + P)
     mf, ms = state_of(n, 3 * k, scale=0.2)
-    codes1, scales1 = orc.encode(x, mf, ms)
+    codes1, scales1 = orc.encode(x, mf, ms, bits=bits)
     e2 = (I.normal(n // P, I.stream_key("e2", k)) * 0.01).astype(np.float32)
     mfd, msd = g.dev(mf), g.dev(ms)
-    st = B.EchoState(mfd, msd, n, P, rank)
+    st = B.EchoState(mfd, msd, n, P, rank, bits=bits)
     B.echo_update(st, g.dev(x), g.dev(codes1), g.dev(scales1), g.dev(e2))
-    orc.update(x, mf, ms, codes1, scales1, e2, P, rank)
+    orc.update(x, mf, ms, codes1, scales1, e2, P, rank, bits=bits)
     eq(g.host(mfd, np.float32), mf, "m_fast")
     eq(g.host(msd, np.float32), ms, "m_slow")
 
 
-def _rank_inputs(P, n, seed, zero_frac=0.02):
+def _rank_inputs(P, n, seed, zero_frac=0.02, bits=4):
     Cn = n // P
-    recv = [None if q is None else I.int4_message(Cn, I.stream_key("recv", seed, q), zero_group_frac=zero_frac)
+    recv = [I.int4_message(Cn, I.stream_key("recv", seed, q), zero_group_frac=zero_frac, bits=bits)
             for q in range(P)]
     gath = [I.int4_message(Cn, I.stream_key("gath", seed, j), scale_lo=0.2, scale_hi=1.5,
-                           zero_group_frac=zero_frac) for j in range(P)]
+                           zero_group_frac=zero_frac, bits=bits) for j in range(P)]
     return recv, gath
 
 
 class RankCase:
     """Device and host copies of one rank-mode problem."""
 
-    def __init__(self, P, rank, k, seed):
+    def __init__(self, P, rank, k, seed, bits=4):
         g = gu()
-        self.P, self.rank = P, rank
+        self.P, self.rank, self.bits = P, rank, bits
         self.n = n = P * 128 * k
         self.Cn = n // P
-        self.recv, self.gath = _rank_inputs(P, n, seed)
+        self.recv, self.gath = _rank_inputs(P, n, seed, bits=bits)
         self.mf = np.zeros(n, np.float32)
         self.ms = np.zeros(n, np.float32)
         self.mfd, self.msd = g.dev(self.mf), g.dev(self.ms)
-        self.st = B.EchoState(self.mfd, self.msd, n, P, rank)
+        self.st = B.EchoState(self.mfd, self.msd, n, P, rank, bits=bits)
         self.recv_d = [(g.dev(c), g.dev(s)) for c, s in self.recv]
         self.gath_d = [(g.dev(c), g.dev(s)) for c, s in self.gath]
-        self.send_c = g.empty_u8(n // 2, 0xAB)
+        self.send_c = g.empty_u8(cb(n, bits), 0xAB)
         self.send_s = g.empty_f32(n // 128, -3.0)
-        self.own_c = g.empty_u8(self.Cn // 2)
+        self.own_c = g.empty_u8(cb(self.Cn, bits))
         self.own_s = g.empty_f32(self.Cn // 128)
         self.y = g.empty_bf16(n)
 
@@ -160,15 +169,17 @@ class RankCase:
 
     def oracle_call(self, x):
         return orc.call(self.P, self.rank, x, self.mf, self.ms, self.slot(self.recv, 0),
-                        self.slot(self.recv, 1), self.slot(self.gath, 0), self.slot(self.gath, 1))
+                        self.slot(self.recv, 1), self.slot(self.gath, 0), self.slot(self.gath, 1),
+                        bits=self.bits)
 
     def check(self, want, y=None):
         g = gu()
         P, r, Cn = self.P, self.rank, self.Cn
         sc = g.host(self.send_c, np.uint8)
         ss = g.host(self.send_s, np.float32)
+        cbc = cb(Cn, self.bits)
         for j in range(P):
-            cs = slice(j * Cn // 2, (j + 1) * Cn // 2)
+            cs = slice(j * cbc, (j + 1) * cbc)
             gs = slice(j * Cn // 128, (j + 1) * Cn // 128)
             if j == r:  # the own chunk of the send buffers is never written
                 assert np.all(sc[cs] == 0xAB) and np.all(ss[gs] == -3.0)
@@ -187,11 +198,12 @@ CALL_SHAPES = [(1, 0, 3), (2, 1, 1), (3, 0, 5), (3, 2, 2), (4, 1, 9), (8, 0, 16)
 
 
 @pytest.mark.parametrize("P,rank,k", CALL_SHAPES)
-def test_call_rank_mode(P, rank, k):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_call_rank_mode(P, rank, k, bits):
     """Fused echo_call over 3 consecutive calls (fresh input each call, the
     averages carried) against the oracle's rank mode."""
     g = gu()
-    case = RankCase(P, rank, k, seed=P * 100 + rank * 10 + k)
+    case = RankCase(P, rank, k, seed=P * 100 + rank * 10 + k, bits=bits)
     for call in range(3):
         x = x_of(case.n, 31 * call + k + P)
         case.gpu_call(g.dev(x))
@@ -224,40 +236,43 @@ def test_phases_equal_fused_call_and_in_place(P, rank, k):
         inplace.check(want, y=xi)
 
 
-@pytest.mark.parametrize("P,rank,k", [(8, 2, 9), (4, 3, 3), (2, 0, 1)])
-def test_fused_equals_unfused_sequence(P, rank, k):
+@pytest.mark.parametrize("P,rank,k,bits", [(8, 2, 9, 4), (4, 3, 3, 4), (2, 0, 1, 4), (8, 6, 5, 8),
+                                           (3, 1, 2, 8)])
+def test_fused_equals_unfused_sequence(P, rank, k, bits):
     """echo_call == echo_encode + echo_reduce_shard (own slot = own encode)
     + echo_decode + echo_update, bit for bit."""
     g = gu()
-    a = RankCase(P, rank, k, seed=5)
-    b = RankCase(P, rank, k, seed=5)
+    a = RankCase(P, rank, k, seed=5, bits=bits)
+    b = RankCase(P, rank, k, seed=5, bits=bits)
     n, Cn = a.n, a.Cn
+    cc = cb(Cn, bits)
     for call in range(3):
         x = x_of(n, 900 + call)
         xd = g.dev(x)
         a.gpu_call(xd)
-        codes1, scales1 = g.empty_u8(n // 2), g.empty_f32(n // 128)
+        codes1, scales1 = g.empty_u8(cb(n, bits)), g.empty_f32(n // 128)
         B.echo_encode(b.st, xd, codes1, scales1)
-        sh_c = [codes1[rank * Cn // 2:(rank + 1) * Cn // 2] if q == rank else b.recv_d[q][0] for q in range(P)]
+        sh_c = [codes1[rank * cc:(rank + 1) * cc] if q == rank else b.recv_d[q][0] for q in range(P)]
         sh_s = [scales1[rank * Cn // 128:(rank + 1) * Cn // 128] if q == rank else b.recv_d[q][1]
                 for q in range(P)]
         e2 = g.empty_f32(Cn)
         codes2 = torch.cat([b.gath_d[j][0] for j in range(P)])
         scales2 = torch.cat([b.gath_d[j][1] for j in range(P)])
-        B.echo_reduce_shard(sh_c, sh_s, codes2[rank * Cn // 2:(rank + 1) * Cn // 2],
-                            scales2[rank * Cn // 128:(rank + 1) * Cn // 128], None, e2, chunk_n=Cn)
+        B.echo_reduce_shard(sh_c, sh_s, codes2[rank * cc:(rank + 1) * cc],
+                            scales2[rank * Cn // 128:(rank + 1) * Cn // 128], None, e2, chunk_n=Cn,
+                            bits=bits)
         y = g.empty_bf16(n)
-        B.echo_decode(codes2, scales2, y)
+        B.echo_decode(codes2, scales2, y, bits=bits)
         B.echo_update(b.st, xd, codes1, scales1, e2)
         eq(g.host(a.y, np.uint16), g.host(y, np.uint16), "y")
-        eq(g.host(a.own_c, np.uint8), g.host(codes2, np.uint8)[rank * Cn // 2:(rank + 1) * Cn // 2], "codes2")
+        eq(g.host(a.own_c, np.uint8), g.host(codes2, np.uint8)[rank * cc:(rank + 1) * cc], "codes2")
         eq(g.host(a.mfd, np.float32), g.host(b.mfd, np.float32), "m_fast")
         eq(g.host(a.msd, np.float32), g.host(b.msd, np.float32), "m_slow")
         sc = g.host(a.send_c, np.uint8)
         c1 = g.host(codes1, np.uint8)
         for j in range(P):
             if j != rank:
-                eq(sc[j * Cn // 2:(j + 1) * Cn // 2], c1[j * Cn // 2:(j + 1) * Cn // 2], "send")
+                eq(sc[j * cc:(j + 1) * cc], c1[j * cc:(j + 1) * cc], "send")
 
 
 def test_state_init_zero_fills():
@@ -335,18 +350,20 @@ def test_full_simulation_small(P, k, calls):
 
 
 @pytest.mark.parametrize("P,rank,k", [(1, 0, 3), (2, 1, 5), (3, 2, 4), (8, 0, 9), (8, 6, 33), (16, 9, 2)])
-def test_call_plain_uncompensated(P, rank, k):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_call_plain_uncompensated(P, rank, k, bits):
     """The uncompensated call against the oracle with compensation off."""
     g = gu()
-    case = RankCase(P, rank, k, seed=300 + P + k)
+    case = RankCase(P, rank, k, seed=300 + P + k, bits=bits)
     n = case.n
     for call in range(2):
         x = x_of(n, 700 + call + k)
         B.echo_call_plain(P, rank, g.dev(x), case.slot(case.recv_d, 0), case.slot(case.recv_d, 1),
                           case.slot(case.gath_d, 0), case.slot(case.gath_d, 1), case.send_c,
-                          case.send_s, case.own_c, case.own_s, case.y)
+                          case.send_s, case.own_c, case.own_s, case.y, bits=bits)
         want = orc.call(P, rank, x, None, None, case.slot(case.recv, 0), case.slot(case.recv, 1),
-                        case.slot(case.gath, 0), case.slot(case.gath, 1), comp=False)
+                        case.slot(case.gath, 0), case.slot(case.gath, 1), comp=False,
+                        bits=bits)
         case.check(want)  # the averages stay untouched (zero), as the oracle's
 
 
@@ -499,21 +516,23 @@ def test_requantizer_decision_boundaries(ulps):
 
 @pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("k", [1, 5, 129])
-def test_reduce_shard_sum(P, k):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_reduce_shard_sum(P, k, bits):
     g = gu()
     cn = 128 * k
-    msgs = [I.int4_message(cn, I.stream_key("rss", P, k, q), zero_group_frac=0.05, any_byte=(q % 2 == 1))
-            for q in range(P)]
+    msgs = [I.int4_message(cn, I.stream_key("rss", P, k, q), zero_group_frac=0.05, any_byte=(q % 2 == 1),
+                           bits=bits) for q in range(P)]
     y, e = g.empty_bf16(cn), g.empty_f32(cn)
-    B.echo_reduce_shard_sum([g.dev(c) for c, _ in msgs], [g.dev(s) for _, s in msgs], y, e, chunk_n=cn)
-    wy, we = orc.reduce_chunk_sum([c for c, _ in msgs], [s for _, s in msgs], cn)
+    B.echo_reduce_shard_sum([g.dev(c) for c, _ in msgs], [g.dev(s) for _, s in msgs], y, e, chunk_n=cn,
+                            bits=bits)
+    wy, we = orc.reduce_chunk_sum([c for c, _ in msgs], [s for _, s in msgs], cn, bits=bits)
     eq(g.host(y, np.uint16), wy, "y")
     eq(g.host(e, np.float32), we, "e")
 
 
 class RsCase(RankCase):
-    def __init__(self, P, rank, k, seed):
-        super().__init__(P, rank, k, seed)
+    def __init__(self, P, rank, k, seed, bits=4):
+        super().__init__(P, rank, k, seed, bits=bits)
         self.y_own = gu().empty_bf16(self.Cn)
 
     def gpu_rs(self, xd):
@@ -522,15 +541,16 @@ class RsCase(RankCase):
 
     def oracle_rs(self, x):
         return orc.rs_call(self.P, self.rank, x, self.mf, self.ms, self.slot(self.recv, 0),
-                           self.slot(self.recv, 1))
+                           self.slot(self.recv, 1), bits=self.bits)
 
     def check_rs(self, want):
         g = gu()
         P, r, Cn = self.P, self.rank, self.Cn
         sc = g.host(self.send_c, np.uint8)
         ss = g.host(self.send_s, np.float32)
+        cbc = cb(Cn, self.bits)
         for j in range(P):
-            cs = slice(j * Cn // 2, (j + 1) * Cn // 2)
+            cs = slice(j * cbc, (j + 1) * cbc)
             gs = slice(j * Cn // 128, (j + 1) * Cn // 128)
             if j == r:
                 assert np.all(sc[cs] == 0xAB) and np.all(ss[gs] == -3.0)
@@ -543,34 +563,36 @@ class RsCase(RankCase):
 
 
 @pytest.mark.parametrize("P,rank,k", [(1, 0, 2), (2, 1, 3), (3, 0, 5), (8, 0, 16), (8, 7, 33), (16, 4, 3)])
-def test_rs_call_rank_mode(P, rank, k):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_rs_call_rank_mode(P, rank, k, bits):
     g = gu()
-    case = RsCase(P, rank, k, seed=400 + P * 10 + rank)
+    case = RsCase(P, rank, k, seed=400 + P * 10 + rank, bits=bits)
     for call in range(3):
         x = x_of(case.n, 800 + call + k)
         case.gpu_rs(g.dev(x))
         case.check_rs(case.oracle_rs(x))
 
 
-@pytest.mark.parametrize("P,rank,k", [(8, 5, 9), (4, 0, 3)])
-def test_rs_fused_equals_unfused(P, rank, k):
+@pytest.mark.parametrize("P,rank,k,bits", [(8, 5, 9, 4), (4, 0, 3, 4), (8, 2, 3, 8)])
+def test_rs_fused_equals_unfused(P, rank, k, bits):
     """echo_rs_call == echo_encode + echo_reduce_shard_sum (own slot = own
     stage-1 chunk) + echo_update, bit for bit, and the phased form too."""
     g = gu()
-    a = RsCase(P, rank, k, seed=9)
-    b = RsCase(P, rank, k, seed=9)
-    c = RsCase(P, rank, k, seed=9)
+    a = RsCase(P, rank, k, seed=9, bits=bits)
+    b = RsCase(P, rank, k, seed=9, bits=bits)
+    c = RsCase(P, rank, k, seed=9, bits=bits)
     n, Cn = a.n, a.Cn
+    cc = cb(Cn, bits)
     for call in range(3):
         xd = g.dev(x_of(n, 60 + call))
         a.gpu_rs(xd)
-        codes1, scales1 = g.empty_u8(n // 2), g.empty_f32(n // 128)
+        codes1, scales1 = g.empty_u8(cb(n, bits)), g.empty_f32(n // 128)
         B.echo_encode(b.st, xd, codes1, scales1)
-        sh_c = [codes1[rank * Cn // 2:(rank + 1) * Cn // 2] if q == rank else b.recv_d[q][0] for q in range(P)]
+        sh_c = [codes1[rank * cc:(rank + 1) * cc] if q == rank else b.recv_d[q][0] for q in range(P)]
         sh_s = [scales1[rank * Cn // 128:(rank + 1) * Cn // 128] if q == rank else b.recv_d[q][1]
                 for q in range(P)]
         e = g.empty_f32(Cn)
-        B.echo_reduce_shard_sum(sh_c, sh_s, b.y_own, e, chunk_n=Cn)
+        B.echo_reduce_shard_sum(sh_c, sh_s, b.y_own, e, chunk_n=Cn, bits=bits)
         B.echo_update(b.st, xd, codes1, scales1, e)
         B.echo_call_entry(c.st, xd, c.send_c, c.send_s)
         B.echo_rs_reduce(c.st, xd, c.slot(c.recv_d, 0), c.slot(c.recv_d, 1), c.y_own)
@@ -606,3 +628,29 @@ def test_rs_full_simulation(P, k, calls):
             eq(g.host(y_own[p], np.uint16), want["y"][p * Cn:(p + 1) * Cn], f"call {call} y rank {p}")
             eq(g.host(r.mf, np.float32), mf[p], f"call {call} m_fast rank {p}")
             eq(g.host(r.ms, np.float32), ms[p], f"call {call} m_slow rank {p}")
+
+
+
+@pytest.mark.parametrize("P,rank,k", [(8, 3, 6), (4, 0, 5)])
+def test_mixed_code_width_sequence(P, rank, k):
+    """The serving policy: one state carried through 8 calls, the first half
+    with 8-bit messages and the second half with 4-bit ones (the width is set
+    on the state before each call), against the oracle call by call."""
+    g = gu()
+    c4 = RankCase(P, rank, k, seed=77, bits=4)
+    c8 = RankCase(P, rank, k, seed=77, bits=8)
+    mfd, msd = c4.mfd, c4.msd
+    mf, ms = c4.mf, c4.ms
+    for call in range(8):
+        bits = 8 if call < 4 else 4
+        c = c8 if bits == 8 else c4
+        st = B.EchoState(mfd, msd, c.n, P, rank, bits=bits)
+        x = x_of(c.n, 5000 + call)
+        B.echo_call(st, g.dev(x), c.slot(c.recv_d, 0), c.slot(c.recv_d, 1), c.slot(c.gath_d, 0),
+                    c.slot(c.gath_d, 1), c.send_c, c.send_s, c.own_c, c.own_s, c.y)
+        want = orc.call(P, rank, x, mf, ms, c.slot(c.recv, 0), c.slot(c.recv, 1), c.slot(c.gath, 0),
+                        c.slot(c.gath, 1), bits=bits)
+        eq(g.host(c.y, np.uint16), want["y"], f"call {call} ({bits}-bit) y")
+        eq(g.host(c.own_c, np.uint8), want["own_codes2"], f"call {call} codes2")
+        eq(g.host(mfd, np.float32), mf, f"call {call} m_fast")
+        eq(g.host(msd, np.float32), ms, f"call {call} m_slow")
