@@ -288,6 +288,123 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
     }
 
 
+WORKLOADS = {
+    # name: (elements per rank, calls per step, description)
+    "tiny": (16 * 4096, 4, "bf16 [16 x 4096] per rank, N(0,1), 0.1% of channels x20; 4 calls per step"),
+    "decode": (256 * 4096, 64, "Llama-3-8B TP=8 decode site: bf16 [256 x 4096] per rank, 0.5 z lambda_c, "
+                               "0.1% of channels x30; 64 calls (32 layers x 2 sites) per step"),
+    "prefill": (8192 * 4096, 1, "Llama-3-8B TP=8 prefill site: bf16 [8192 x 4096] per rank; one call "
+                                "on warm state per step"),
+    "train": (8 * 4096 * 1024, 112, "Qwen3-0.6B TP=8 training step: bf16 [8 x 4096 x 1024]; 56 forward "
+                                    "calls on one state, 56 backward calls (1e-3 Student-t(3)) on another"),
+}
+
+
+def run_workload(args) -> int:
+    """Per-rank timing of the smaller workloads (rank 0 of P = 8): a step is
+    the workload's whole call sequence; inputs differ call to call.  With
+    --graph the step is also captured once in a HIP graph and replayed."""
+    import numpy as np
+    import torch
+
+    from error_compensated_bit_echo_amd import binding as B
+    from error_compensated_bit_echo_amd import inputs as I
+
+    n, calls, desc = WORKLOADS[args.workload]
+    P, rank = 8, 0
+    C = n // P
+    dev = torch.device("cuda:0")
+    print(f"bench: workload {args.workload}: n={n}, {calls} calls per step", file=sys.stderr, flush=True)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    # inputs, one per call of a step
+    if args.workload == "tiny":
+        ck = I.stream_key("tiny", "channels")
+        xs = [d(I.gaussian_outlier_channels(16, 4096, I.stream_key("tiny", c), channel_key=ck))
+              for c in range(calls)]
+    elif args.workload in ("decode", "prefill"):
+        ck = I.stream_key(args.workload, "channels")
+        rows = n // 4096
+        xs = [d(I.lognormal_channel_activations(rows, 4096, I.stream_key(args.workload, c), ck))
+              for c in range(calls)]
+    else:
+        lam = I.channel_scales(1024, I.stream_key("train", "channels"))
+        xs = [I.device_lognormal_channel_activations(n // 1024, 1024, 1000 + c, lam, dev)
+              for c in range(calls // 2)]
+        xs += [I.device_student_t3(n, 2000 + c, dev) for c in range(calls // 2)]
+    recv = [None if q == rank else tuple(d(t) for t in I.int4_message(C, I.stream_key("w-recv", q)))
+            for q in range(P)]
+    gath = [None if j == rank else tuple(d(t) for t in I.int4_message(C, I.stream_key("w-gath", j),
+                                                                      scale_lo=0.15, scale_hi=1.5))
+            for j in range(P)]
+    rc_ = [None if m is None else m[0] for m in recv]
+    rs_ = [None if m is None else m[1] for m in recv]
+    gc_ = [None if m is None else m[0] for m in gath]
+    gs_ = [None if m is None else m[1] for m in gath]
+    nstates = 2 if args.workload == "train" else 1
+    mem = [(torch.empty(n, device=dev), torch.empty(n, device=dev)) for _ in range(nstates)]
+    stream = torch.cuda.current_stream()
+    states = [B.echo_state_init(a, b, n, P, rank, stream) for a, b in mem]
+    send_c = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    send_s = torch.empty(n // 128, dtype=torch.float32, device=dev)
+    own_c = torch.empty(C // 2, dtype=torch.uint8, device=dev)
+    own_s = torch.empty(C // 128, dtype=torch.float32, device=dev)
+    ys = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(calls)]
+
+    def step():
+        s = torch.cuda.current_stream()
+        for c in range(calls):
+            st = states[0] if c < calls // nstates or nstates == 1 else states[1]
+            B.echo_call(st, xs[c], rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, ys[c], s)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    graph_ms = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()  # warm the side stream before capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    best = min(eager_ms, graph_ms) if graph_ms else eager_ms
+    per_call = step_bytes(n, P)
+    out = {
+        "metric": METRIC, "value": round(2.0 * n * calls / (best * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(best, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {desc}", "elements": n, "nranks": P, "rank": rank,
+                   "calls_per_step": calls},
+        "us_per_call": round(best * 1e3 / calls, 2),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "pct_hbm_peak": round(100.0 * per_call * calls / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "algorithmic_bytes_per_call": int(per_call),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,12 +420,18 @@ def main() -> int:
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) before the warmup, as "
                          "the known-size reference for HBM counter runs")
+    ap.add_argument("--workload", default="1gb", choices=["1gb", *WORKLOADS],
+                    help="1gb (the headline, default) or one of the smaller workloads")
+    ap.add_argument("--graph", action="store_true",
+                    help="smaller workloads: also time the step captured in a HIP graph")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print("bench.py measures the per-rank pipeline on one GPU; this build has no "
               "multi-GPU transport, so --gpus must be 1", file=sys.stderr)
         return 2
+    if args.workload != "1gb":
+        return run_workload(args)
 
     import numpy as np
     import torch
