@@ -654,3 +654,29 @@ def test_mixed_code_width_sequence(P, rank, k):
         eq(g.host(c.own_c, np.uint8), want["own_codes2"], f"call {call} codes2")
         eq(g.host(mfd, np.float32), mf, f"call {call} m_fast")
         eq(g.host(msd, np.float32), ms, f"call {call} m_slow")
+
+
+def test_checkpoint_resume_is_bit_identical():
+    """The averages are the only state carried between calls: saving them
+    after k calls and continuing from the saved copy in fresh buffers (as a
+    checkpoint restore would) gives exactly the uninterrupted run."""
+    g = gu()
+    P, rank, k = 8, 2, 7
+    whole = RankCase(P, rank, k, seed=91)
+    xs = [x_of(whole.n, 9100 + c) for c in range(6)]
+    for c in range(3):
+        whole.gpu_call(g.dev(xs[c]))
+    torch.cuda.synchronize()
+    saved_mf = g.host(whole.mfd, np.float32).copy()  # the checkpoint, on the host
+    saved_ms = g.host(whole.msd, np.float32).copy()
+    for c in range(3, 6):
+        whole.gpu_call(g.dev(xs[c]))
+    resumed = RankCase(P, rank, k, seed=91)
+    resumed.mfd.copy_(g.dev(saved_mf))
+    resumed.msd.copy_(g.dev(saved_ms))
+    for c in range(3, 6):
+        resumed.gpu_call(g.dev(xs[c]))
+    torch.cuda.synchronize()
+    eq(g.host(resumed.y, np.uint16), g.host(whole.y, np.uint16), "y after resume")
+    eq(g.host(resumed.mfd, np.float32), g.host(whole.mfd, np.float32), "m_fast after resume")
+    eq(g.host(resumed.msd, np.float32), g.host(whole.msd, np.float32), "m_slow after resume")
