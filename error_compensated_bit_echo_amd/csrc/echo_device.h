@@ -33,7 +33,10 @@ constexpr int kGroup = ECHO_GROUP;
 template <int BITS>
 __host__ __device__ constexpr float qmax_of() { return BITS == 8 ? (float)ECHO_QMAX8 : (float)ECHO_QMAX; }
 constexpr int kMaxRanks = ECHO_MAX_RANKS;
-constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts)
+#ifndef ECHO_BLOCK
+#define ECHO_BLOCK 256
+#endif
+constexpr int kBlock = ECHO_BLOCK;  // threads per workgroup (4 wavefronts)
 
 // Cache policy of the streaming accesses: every byte of the averages, the
 // input and the messages is touched once per call, so loads and stores of
