@@ -10,7 +10,8 @@
 // access of a wave is one contiguous run (x: 512 B, each average: 1 KiB,
 // codes: 128 B) and a group's absmax is a 32-lane reduction done with DPP
 // row operations plus one ds_swizzle (no LDS traffic, no barrier).  The exit
-// kernel gives each lane 8 elements (a group is one 16-lane DPP row).
+// kernel gives each lane 8 elements (a group is 16 lanes) and needs no
+// reduction.
 //
 // Arithmetic.  Built with -ffp-contract=off: each float operation below is
 // one IEEE binary32 operation rounded to nearest even, denormals kept;
@@ -99,15 +100,6 @@ __device__ __forceinline__ uint32_t halfwave_max(uint32_t v) {
   v = max(v, dpp_u32<0x140>(v));  // row_mirror: half-row 0 <-> half-row 1
   // bitmask swizzle (and 0x1F, or 0, xor 0x10): row 0 <-> row 1 in each 32
   v = max(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));
-  return v;
-}
-
-// max over each 16-lane row (all 64 lanes must be active).
-__device__ __forceinline__ uint32_t row_max(uint32_t v) {
-  v = max(v, dpp_u32<0xB1>(v));
-  v = max(v, dpp_u32<0x4E>(v));
-  v = max(v, dpp_u32<0x141>(v));
-  v = max(v, dpp_u32<0x140>(v));
   return v;
 }
 
