@@ -97,13 +97,16 @@ def _ptr(t):
     return t.data_ptr()
 
 
+_PTR16 = C.c_void_p * MAX_RANKS
+
+
 def _ptrs(ts):
-    # at least MAX_RANKS slots: entries past the list are NULL, which the
-    # library rejects instead of reading past the array
-    arr = (C.c_void_p * max(MAX_RANKS, len(ts)))()
-    for i, t in enumerate(ts):
-        arr[i] = _ptr(t)
-    return C.cast(arr, _pp)
+    """void*[>= MAX_RANKS] of device addresses: entries past the list are NULL,
+    which the library rejects instead of reading past the array."""
+    vals = [None if t is None else (t if isinstance(t, int) else t.data_ptr()) for t in ts]
+    if len(vals) <= MAX_RANKS:
+        return _PTR16(*vals)
+    return (C.c_void_p * len(vals))(*vals)
 
 
 def _stream(stream):
@@ -233,6 +236,35 @@ def echo_rs_call(st: EchoState, x, recv_codes, recv_scales, send_codes, send_sca
     _check(lib.echo_rs_call(C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
                             _ptr(send_codes), _ptr(send_scales), _ptr(y_own), _stream(stream)),
            "echo_rs_call")
+
+
+class PreparedCall:
+    """echo_call with every argument marshalled once: for loops that call the
+    pipeline again and again on the same buffers (a serving loop's per-layer
+    buffers).  Calling it enqueues the call on `stream` (default: torch's
+    current stream).  The tensors are kept alive by this object; their
+    contents may change between calls, their storage may not."""
+
+    def __init__(self, st: EchoState, x, recv_codes, recv_scales, gath_codes, gath_scales,
+                 send_codes, send_scales, own_codes2, own_scales2, y):
+        self._keep = (st, x, recv_codes, recv_scales, gath_codes, gath_scales, send_codes,
+                      send_scales, own_codes2, own_scales2, y)
+        self._args = (C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
+                      _ptrs(gath_codes), _ptrs(gath_scales), _ptr(send_codes), _ptr(send_scales),
+                      _ptr(own_codes2), _ptr(own_scales2), _ptr(y))
+        self._fn = lib.echo_call
+
+    def __call__(self, stream=None) -> None:
+        rc = self._fn(*self._args, _stream(stream))
+        if rc != 0:
+            raise EchoError(rc, "echo_call")
+
+
+def echo_call_prepare(st: EchoState, x, recv_codes, recv_scales, gath_codes, gath_scales,
+                      send_codes, send_scales, own_codes2, own_scales2, y) -> PreparedCall:
+    """A reusable echo_call on fixed buffers (see PreparedCall)."""
+    return PreparedCall(st, x, recv_codes, recv_scales, gath_codes, gath_scales, send_codes,
+                        send_scales, own_codes2, own_scales2, y)
 
 
 def echo_get_config() -> dict:

@@ -680,3 +680,31 @@ def test_checkpoint_resume_is_bit_identical():
     eq(g.host(resumed.y, np.uint16), g.host(whole.y, np.uint16), "y after resume")
     eq(g.host(resumed.mfd, np.float32), g.host(whole.mfd, np.float32), "m_fast after resume")
     eq(g.host(resumed.msd, np.float32), g.host(whole.msd, np.float32), "m_slow after resume")
+
+
+def test_prepared_call_matches_echo_call():
+    """echo_call_prepare marshals the arguments once; each call of it is the
+    same echo_call on the buffers' current contents."""
+    g = gu()
+    P, rank, k = 8, 4, 5
+    a = RankCase(P, rank, k, seed=33)
+    b = RankCase(P, rank, k, seed=33)
+    xb = g.dev(np.zeros(b.n, np.uint16))
+    prepared = B.echo_call_prepare(b.st, xb, b.slot(b.recv_d, 0), b.slot(b.recv_d, 1),
+                                   b.slot(b.gath_d, 0), b.slot(b.gath_d, 1), b.send_c, b.send_s,
+                                   b.own_c, b.own_s, b.y)
+    side = torch.cuda.Stream()
+    for call in range(4):
+        x = x_of(a.n, 3300 + call)
+        a.gpu_call(g.dev(x))
+        xb.copy_(g.dev(x))
+        if call % 2:
+            prepared()
+        else:  # an explicit stream, ordered after the input copy
+            side.wait_stream(torch.cuda.current_stream())
+            prepared(side)
+            torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        eq(g.host(b.y, np.uint16), g.host(a.y, np.uint16), f"call {call} y")
+        eq(g.host(b.mfd, np.float32), g.host(a.mfd, np.float32), f"call {call} m_fast")
+        eq(g.host(b.own_c, np.uint8), g.host(a.own_c, np.uint8), f"call {call} codes2")
