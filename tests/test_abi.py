@@ -192,3 +192,8 @@ def test_code_width_rejections():
     # (n/2 = 512 bytes from x - 1008) reach 16 bytes into x in 8-bit form
     s8.bits = 8
     assert rc(B.echo_encode, s8, 3 * A, 3 * A - 1008, 5 * A) == -6
+
+
+def test_build_entry_check_matches_header():
+    import __graft_entry__ as ge
+    ge.check_loaded()
