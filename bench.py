@@ -300,6 +300,19 @@ WORKLOADS = {
 }
 
 
+def calibration_copy(dev) -> None:
+    """A plain device copy of known size (reads 1 GiB, writes 1 GiB): the
+    reference that scales HBM counter readings to bytes."""
+    import torch
+
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_workload(args) -> int:
     """Per-rank timing of the smaller workloads (rank 0 of P = 8): a step is
     the workload's whole call sequence; inputs differ call to call.  With
@@ -335,11 +348,11 @@ def run_workload(args) -> int:
         xs = [I.device_lognormal_channel_activations(n // 1024, 1024, 1000 + c, lam, dev)
               for c in range(calls // 2)]
         xs += [I.device_student_t3(n, 2000 + c, dev) for c in range(calls // 2)]
-    recv = [None if q == rank else tuple(d(t) for t in I.int4_message(C, I.stream_key("w-recv", q)))
-            for q in range(P)]
-    gath = [None if j == rank else tuple(d(t) for t in I.int4_message(C, I.stream_key("w-gath", j),
-                                                                      scale_lo=0.15, scale_hi=1.5))
-            for j in range(P)]
+    recv_h = [None if q == rank else I.int4_message(C, I.stream_key("w-recv", q)) for q in range(P)]
+    gath_h = [None if j == rank else I.int4_message(C, I.stream_key("w-gath", j), scale_lo=0.15, scale_hi=1.5)
+              for j in range(P)]
+    recv = [None if m is None else tuple(d(t) for t in m) for m in recv_h]
+    gath = [None if m is None else tuple(d(t) for t in m) for m in gath_h]
     rc_ = [None if m is None else m[0] for m in recv]
     rs_ = [None if m is None else m[1] for m in recv]
     gc_ = [None if m is None else m[0] for m in gath]
@@ -363,6 +376,9 @@ def run_workload(args) -> int:
         s = torch.cuda.current_stream()
         for pc in prepared:
             pc(s)
+
+    if args.calibrate:
+        calibration_copy(dev)
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -405,8 +421,42 @@ def run_workload(args) -> int:
         "pct_hbm_peak": round(100.0 * per_call * calls / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "algorithmic_bytes_per_call": int(per_call),
     }
+    out["cpu_baseline"] = None if args.no_cpu else workload_cpu_baseline(
+        xs, recv_h, gath_h, P, rank, nstates, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def workload_cpu_baseline(xs, recv_h, gath_h, P: int, rank: int, nstates: int, budget_s: float):
+    """The CPU oracle as it stands (one thread) on the workload's own call
+    sequence: the step's calls in order, from zero state (one state per
+    direction for the training step), until the step ends or about
+    budget_s seconds have passed; payload GB/s."""
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    n = int(xs[0].numel())
+    calls = len(xs)
+    sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
+    rc, rs, gc, gs = sl(recv_h, 0), sl(recv_h, 1), sl(gath_h, 0), sl(gath_h, 1)
+    states = [(np.zeros(n, np.float32), np.zeros(n, np.float32)) for _ in range(nstates)]
+    done, spent = 0, 0.0
+    while done < calls and spent < budget_s:
+        x = xs[done].cpu().numpy().view(np.uint16)
+        mf, ms = states[0] if nstates == 1 or done < calls // nstates else states[1]
+        t0 = time.perf_counter()
+        orc.call(P, rank, x, mf, ms, rc, rs, gc, gs)
+        spent += time.perf_counter() - t0
+        done += 1
+    return {
+        "value": round(2.0 * n * done / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"the first {done} of the step's {calls} rank-mode calls (P={P}, rank {rank}), "
+                  f"{n} elements each, state carried; {spent:.2f} s on one host thread",
+    }
 
 
 def main() -> int:
@@ -419,6 +469,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-log2n", type=int, default=26)
     ap.add_argument("--cpu-calls", type=int, default=24)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="smaller workloads: CPU time budget of the oracle leg")
     ap.add_argument("--no-schedules", action="store_true",
                     help="skip the critical-path comparison (fused / split / uncompensated)")
     ap.add_argument("--calibrate", action="store_true",
@@ -483,13 +535,7 @@ def main() -> int:
             ev[3].record(stream)
 
     if args.calibrate:
-        # a plain copy of known size: reads 1 GiB and writes 1 GiB
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(dev)
     print(f"bench: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
