@@ -61,18 +61,31 @@ bool bits_ok(int32_t bits) { return bits == 4 || bits == 8; }
 // bytes of the codes of n elements: packed nibbles, or one byte per code
 int64_t code_bytes(int64_t n, int32_t bits) { return bits == 8 ? n : n / 2; }
 
+// A check that passed with nothing to do: zero elements.  The entry point
+// then returns ECHO_SUCCESS without looking at its pointers or launching.
+constexpr int kEmpty = 1;
+
+// the status an entry point returns for a check result that is not SUCCESS
+int finished(int rc) { return rc < 0 ? rc : ECHO_SUCCESS; }
+
+int check_elements(int64_t n, int64_t multiple) {
+  if (n < 0 || n > ECHO_MAX_ELEMENTS || n % multiple != 0) return ECHO_ERR_SHAPE;
+  return n == 0 ? kEmpty : ECHO_SUCCESS;
+}
+
 int check_ranks_shape(int64_t n, int32_t P) {
   if (P < 1 || P > ECHO_MAX_RANKS) return ECHO_ERR_RANKS;
-  if (n <= 0 || n > ECHO_MAX_ELEMENTS || n % ((int64_t)P * ECHO_GROUP) != 0) return ECHO_ERR_SHAPE;
-  return ECHO_SUCCESS;
+  return check_elements(n, (int64_t)P * ECHO_GROUP);
 }
 
 int check_state(const echo_state* st) {
-  if (!st || !st->m_fast || !st->m_slow) return ECHO_ERR_INVALID_ARGUMENT;
-  int rc = check_ranks_shape(st->n, st->nranks);
-  if (rc) return rc;
+  if (!st) return ECHO_ERR_INVALID_ARGUMENT;
+  const int shape = check_ranks_shape(st->n, st->nranks);
+  if (shape < 0) return shape;
   if (st->rank < 0 || st->rank >= st->nranks) return ECHO_ERR_RANKS;
   if (!bits_ok(st->bits)) return ECHO_ERR_FORMAT;
+  if (shape == kEmpty) return kEmpty;
+  if (!st->m_fast || !st->m_slow) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(st->m_fast, 16) || !aligned(st->m_slow, 16)) return ECHO_ERR_ALIGNMENT;
   return ECHO_SUCCESS;
 }
@@ -354,11 +367,14 @@ extern "C" {
 
 int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int32_t nranks,
                     int32_t rank, echo_stream_t stream) {
-  if (!st || !m_fast || !m_slow) return ECHO_ERR_INVALID_ARGUMENT;
-  int rc = check_ranks_shape(n, nranks);
-  if (rc) return rc;
+  if (!st) return ECHO_ERR_INVALID_ARGUMENT;
+  const int shape = check_ranks_shape(n, nranks);
+  if (shape < 0) return shape;
   if (rank < 0 || rank >= nranks) return ECHO_ERR_RANKS;
-  if (!aligned(m_fast, 16) || !aligned(m_slow, 16)) return ECHO_ERR_ALIGNMENT;
+  if (shape != kEmpty) {
+    if (!m_fast || !m_slow) return ECHO_ERR_INVALID_ARGUMENT;
+    if (!aligned(m_fast, 16) || !aligned(m_slow, 16)) return ECHO_ERR_ALIGNMENT;
+  }
   Aliases al;
   al.out(m_fast, n * 4);
   al.out(m_slow, n * 4);
@@ -370,6 +386,7 @@ int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int
   st->rank = rank;
   st->bits = 4;
   st->reserved = 0;
+  if (shape == kEmpty) return ECHO_SUCCESS;
   const int64_t n4 = n / 4;
   int64_t blocks = (n4 + kBlock - 1) / kBlock;
   if (blocks > (int64_t)kMaxBlocks) blocks = kMaxBlocks;
@@ -381,7 +398,7 @@ int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int
 int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* scales,
                 echo_stream_t stream) {
   int rc = check_state(st);
-  if (rc) return rc;
+  if (rc) return finished(rc);
   if (!x || !codes || !scales) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4)) return ECHO_ERR_ALIGNMENT;
   const int64_t n = st->n;
@@ -410,7 +427,8 @@ int echo_reduce_shard(int32_t nranks, int64_t chunk_n, int32_t bits,
                       echo_stream_t stream) {
   if (nranks < 1 || nranks > ECHO_MAX_RANKS) return ECHO_ERR_RANKS;
   if (!bits_ok(bits)) return ECHO_ERR_FORMAT;
-  if (chunk_n <= 0 || chunk_n > ECHO_MAX_ELEMENTS || chunk_n % ECHO_GROUP != 0) return ECHO_ERR_SHAPE;
+  const int shape = check_elements(chunk_n, ECHO_GROUP);
+  if (shape) return finished(shape);
   if (!shard_codes || !shard_scales || !out_codes || !out_scales) return ECHO_ERR_INVALID_ARGUMENT;
   for (int q = 0; q < nranks; ++q) {
     if (!shard_codes[q] || !shard_scales[q]) return ECHO_ERR_INVALID_ARGUMENT;
@@ -446,8 +464,10 @@ int echo_reduce_shard(int32_t nranks, int64_t chunk_n, int32_t bits,
 
 int echo_decode(int64_t n, int32_t bits, const uint8_t* codes, const float* scales, uint16_t* y,
                 echo_stream_t stream) {
-  if (n <= 0 || n > ECHO_MAX_ELEMENTS || n % ECHO_GROUP != 0) return ECHO_ERR_SHAPE;
+  const int shape = check_elements(n, ECHO_GROUP);
+  if (shape < 0) return shape;
   if (!bits_ok(bits)) return ECHO_ERR_FORMAT;
+  if (shape == kEmpty) return ECHO_SUCCESS;
   if (!codes || !scales || !y) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(codes, 16) || !aligned(scales, 4) || !aligned(y, 16)) return ECHO_ERR_ALIGNMENT;
   Aliases al;
@@ -467,7 +487,7 @@ int echo_decode(int64_t n, int32_t bits, const uint8_t* codes, const float* scal
 int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
                 const float* scales1, const float* e2_own, echo_stream_t stream) {
   int rc = check_state(st);
-  if (rc) return rc;
+  if (rc) return finished(rc);
   if (!x || !codes1 || !scales1 || !e2_own) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(codes1, 16) || !aligned(scales1, 4) || !aligned(e2_own, 16))
     return ECHO_ERR_ALIGNMENT;
@@ -496,7 +516,7 @@ int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
 int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes,
                     float* send_scales, echo_stream_t stream) {
   int rc = check_state(st);
-  if (rc) return rc;
+  if (rc) return finished(rc);
   if (!x || !send_codes || !send_scales) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(send_codes, 16) || !aligned(send_scales, 4))
     return ECHO_ERR_ALIGNMENT;
@@ -515,7 +535,7 @@ int echo_call_reduce(const echo_state* st, const uint16_t* x, const uint8_t* con
                      const float* const* recv_scales, uint8_t* own_codes2, float* own_scales2,
                      uint16_t* y, echo_stream_t stream) {
   int rc = check_state(st);
-  if (rc) return rc;
+  if (rc) return finished(rc);
   if (!x || !own_codes2 || !own_scales2 || !y) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(own_codes2, 16) || !aligned(own_scales2, 4) || !aligned(y, 16))
     return ECHO_ERR_ALIGNMENT;
@@ -539,7 +559,7 @@ int echo_call_reduce(const echo_state* st, const uint16_t* x, const uint8_t* con
 int echo_call_exit(const echo_state* st, const uint8_t* const* gath_codes,
                    const float* const* gath_scales, uint16_t* y, echo_stream_t stream) {
   int rc = check_state(st);
-  if (rc) return rc;
+  if (rc) return finished(rc);
   if (!y) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(y, 16)) return ECHO_ERR_ALIGNMENT;
   rc = check_remote_arrays(st, gath_codes, gath_scales);
@@ -559,7 +579,7 @@ int echo_call(const echo_state* st, const uint16_t* x, const uint8_t* const* rec
               const float* const* gath_scales, uint8_t* send_codes, float* send_scales,
               uint8_t* own_codes2, float* own_scales2, uint16_t* y, echo_stream_t stream) {
   int rc = check_state(st);
-  if (rc) return rc;
+  if (rc) return finished(rc);
   if (!x || !send_codes || !send_scales || !own_codes2 || !own_scales2 || !y)
     return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(send_codes, 16) || !aligned(send_scales, 4) ||
@@ -597,9 +617,10 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, int32_t bits, const
                     uint8_t* send_codes, float* send_scales, uint8_t* own_codes2,
                     float* own_scales2, uint16_t* y, echo_stream_t stream) {
   int rc = check_ranks_shape(n, nranks);
-  if (rc) return rc;
+  if (rc < 0) return rc;
   if (rank < 0 || rank >= nranks) return ECHO_ERR_RANKS;
   if (!bits_ok(bits)) return ECHO_ERR_FORMAT;
+  if (rc == kEmpty) return ECHO_SUCCESS;
   if (!x || !send_codes || !send_scales || !own_codes2 || !own_scales2 || !y)
     return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(send_codes, 16) || !aligned(send_scales, 4) ||
@@ -643,7 +664,8 @@ int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, int32_t bits,
                           uint16_t* out_y, float* out_e2, echo_stream_t stream) {
   if (nranks < 1 || nranks > ECHO_MAX_RANKS) return ECHO_ERR_RANKS;
   if (!bits_ok(bits)) return ECHO_ERR_FORMAT;
-  if (chunk_n <= 0 || chunk_n > ECHO_MAX_ELEMENTS || chunk_n % ECHO_GROUP != 0) return ECHO_ERR_SHAPE;
+  const int shape = check_elements(chunk_n, ECHO_GROUP);
+  if (shape) return finished(shape);
   if (!shard_codes || !shard_scales || !out_y) return ECHO_ERR_INVALID_ARGUMENT;
   for (int q = 0; q < nranks; ++q) {
     if (!shard_codes[q] || !shard_scales[q]) return ECHO_ERR_INVALID_ARGUMENT;
@@ -674,7 +696,7 @@ int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, int32_t bits,
 int echo_rs_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
                    const float* const* recv_scales, uint16_t* y_own, echo_stream_t stream) {
   int rc = check_state(st);
-  if (rc) return rc;
+  if (rc) return finished(rc);
   Aliases al;
   rc = check_rs_reduce(st, x, recv_codes, recv_scales, y_own, al);
   if (rc) return rc;
@@ -688,7 +710,7 @@ int echo_rs_call(const echo_state* st, const uint16_t* x, const uint8_t* const* 
                  const float* const* recv_scales, uint8_t* send_codes, float* send_scales,
                  uint16_t* y_own, echo_stream_t stream) {
   int rc = check_state(st);
-  if (rc) return rc;
+  if (rc) return finished(rc);
   if (!send_codes || !send_scales) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(send_codes, 16) || !aligned(send_scales, 4)) return ECHO_ERR_ALIGNMENT;
   Aliases al;
@@ -727,7 +749,7 @@ const char* echo_status_string(int status) {
   switch (status) {
     case ECHO_SUCCESS: return "success";
     case ECHO_ERR_INVALID_ARGUMENT: return "invalid argument (NULL pointer)";
-    case ECHO_ERR_SHAPE: return "bad shape (n must be > 0, a multiple of P*128, within the limit)";
+    case ECHO_ERR_SHAPE: return "bad shape (n must be >= 0, a multiple of P*128, within the limit)";
     case ECHO_ERR_ALIGNMENT: return "misaligned pointer (16 bytes for tensors/codes, 4 for scales)";
     case ECHO_ERR_RANKS: return "bad rank count or rank index";
     case ECHO_ERR_HIP: return "HIP runtime error";

@@ -53,9 +53,15 @@
  *     the enqueued work completes.
  *   - Alignment: bf16 tensors, codes, averages and e2 arrays must be 16-byte
  *     aligned; scale arrays 4-byte aligned (ECHO_ERR_ALIGNMENT).
- *   - Shapes: n > 0, n % (P*128) == 0, n <= ECHO_MAX_ELEMENTS
+ *   - Shapes: 0 <= n <= ECHO_MAX_ELEMENTS and n % (P*128) == 0
  *     (ECHO_ERR_SHAPE); 1 <= P <= ECHO_MAX_RANKS and 0 <= rank < P
- *     (ECHO_ERR_RANKS).
+ *     (ECHO_ERR_RANKS).  A tensor whose length is not a whole number of
+ *     groups per chunk is padded by the caller (a zero tail quantizes to
+ *     zero codes and leaves its averages at zero).
+ *   - Empty calls: n == 0 (chunk_n == 0 for the stateless calls) is a
+ *     no-op.  The scalar arguments (P, rank, bits) are still checked, the
+ *     pointer arguments are not looked at (NULL is fine), nothing is
+ *     enqueued and ECHO_SUCCESS is returned.
  *   - Aliasing: outputs may not overlap each other or any input
  *     (ECHO_ERR_ALIAS), except that y may equal x exactly (in place) where
  *     a call takes both; with the phased calls below, run the exit pass

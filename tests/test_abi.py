@@ -81,7 +81,7 @@ def test_state_init_rejections():
     assert L.echo_state_init(None, A, 2 * A, 1024, 2, 0, None) == -1
     assert L.echo_state_init(C.byref(s), None, 2 * A, 1024, 2, 0, None) == -1
     assert L.echo_state_init(C.byref(s), A, 2 * A, 1000, 2, 0, None) == -2
-    assert L.echo_state_init(C.byref(s), A, 2 * A, 0, 2, 0, None) == -2
+    assert L.echo_state_init(C.byref(s), A, 2 * A, -1024, 2, 0, None) == -2
     assert L.echo_state_init(C.byref(s), A, 2 * A, 128, 2, 0, None) == -2   # n % (P*128)
     assert L.echo_state_init(C.byref(s), A, 2 * A, 1024, 0, 0, None) == -4
     assert L.echo_state_init(C.byref(s), A, 2 * A, 1024 * 17, 17, 0, None) == -4
@@ -192,6 +192,43 @@ def test_code_width_rejections():
     # (n/2 = 512 bytes from x - 1008) reach 16 bytes into x in 8-bit form
     s8.bits = 8
     assert rc(B.echo_encode, s8, 3 * A, 3 * A - 1008, 5 * A) == -6
+
+
+def test_empty_calls_are_noops():
+    """n == 0 (chunk_n == 0): scalar arguments are checked, pointers are not
+    looked at, nothing is launched (so no GPU is touched here), success."""
+    L = B.lib
+    s = B.EchoStateC()
+    assert L.echo_state_init(C.byref(s), None, None, 0, 8, 3, None) == 0
+    assert (s.n, s.nranks, s.rank, s.bits) == (0, 8, 3, 4)
+    assert L.echo_state_init(C.byref(s), None, None, 0, 8, 8, None) == -4
+    assert L.echo_state_init(C.byref(s), None, None, 0, 17, 0, None) == -4
+    assert L.echo_state_init(None, None, None, 0, 8, 0, None) == -1
+    e = B.EchoState(None, None, 0, 8, 3)
+    nulls = [None] * 8
+    B.echo_encode(e, None, None, None, stream=0)
+    B.echo_update(e, None, None, None, None, stream=0)
+    B.echo_call_entry(e, None, None, None, stream=0)
+    B.echo_call_reduce(e, None, nulls, nulls, None, None, None, stream=0)
+    B.echo_call_exit(e, nulls, nulls, None, stream=0)
+    B.echo_call(e, None, nulls, nulls, nulls, nulls, None, None, None, None, None, stream=0)
+    B.echo_rs_reduce(e, None, nulls, nulls, None, stream=0)
+    B.echo_rs_call(e, None, nulls, nulls, None, None, None, stream=0)
+    B.echo_call_plain(8, 3, None, nulls, nulls, nulls, nulls, None, None, None, None, None, 0, stream=0)
+    B.echo_reduce_shard(nulls, nulls, None, None, None, None, 0, stream=0)
+    B.echo_reduce_shard_sum(nulls, nulls, None, None, 0, stream=0)
+    B.echo_decode(None, None, None, 0, stream=0)
+    B.echo_decode(None, None, None, 0, bits=8, stream=0)
+    # the scalar checks still apply to an empty call
+    e.bits = 5
+    assert rc(B.echo_call, e, None, nulls, nulls, nulls, nulls, None, None, None, None, None) == -7
+    assert rc(B.echo_call, B.EchoState(None, None, 0, 8, 9), None, nulls, nulls, nulls, nulls,
+              None, None, None, None, None) == -4
+    assert rc(B.echo_call_plain, 0, 0, None, [], [], [], [], None, None, None, None, None, 0) == -4
+    assert rc(B.echo_decode, None, None, None, 0, bits=3) == -7
+    assert rc(B.echo_decode, None, None, None, -128) == -2
+    assert rc(B.echo_reduce_shard, nulls * 3, nulls * 3, None, None, None, None, 0) == -4
+    assert rc(B.echo_reduce_shard_sum, nulls, nulls, None, None, 0, bits=2) == -7
 
 
 def test_build_entry_check_matches_header():

@@ -349,6 +349,56 @@ def test_full_simulation_small(P, k, calls):
             eq(g.host(r.ms, np.float32), ms[p], f"m_slow rank {p}")
 
 
+def test_zero_padded_tail_full_simulation():
+    """A tensor padded with zeros to whole groups per chunk (the tail spans
+    the last chunk and part of the one before): the GPU matches the oracle's
+    simulation, and the tail's outputs and averages stay zero."""
+    g = gu()
+    P, n, real = 4, 1536, 1036
+    mf = [np.zeros(n, np.float32) for _ in range(P)]
+    ms = [np.zeros(n, np.float32) for _ in range(P)]
+    ranks = [g.GpuRank(np.zeros(n, np.uint16), mf[p], ms[p], P, p) for p in range(P)]
+    for call in range(3):
+        xs = [np.concatenate([I.to_bf16_bits(I.normal(real, I.stream_key("pad", call, p)) * (1 + p)),
+                              np.zeros(n - real, np.uint16)]) for p in range(P)]
+        codes2, scales2, _, _ = g.gpu_simulate_call(ranks, xs)
+        want = orc.simulate(xs, mf, ms)
+        eq(g.host(codes2, np.uint8), want["codes2"], f"call {call} codes2")
+        for p, r in enumerate(ranks):
+            eq(g.host(r.y, np.uint16), want["y"], f"call {call} y rank {p}")
+            eq(g.host(r.mf, np.float32), mf[p], f"call {call} m_fast rank {p}")
+            eq(g.host(r.ms, np.float32), ms[p], f"call {call} m_slow rank {p}")
+            assert not g.host(r.y, np.uint16)[real:].any()
+            assert not g.host(r.mf, np.float32)[real:].view(np.uint32).any()
+
+
+def test_empty_calls_touch_nothing():
+    """n == 0: every entry point returns success and writes nothing, with
+    empty tensors (NULL pointers) or with real buffers passed in."""
+    g = gu()
+    P, rank = 8, 2
+    empty = torch.empty(0, dtype=torch.uint8, device=g.DEV)
+    st = B.echo_state_init(empty, empty, 0, P, rank)
+    assert st.n == 0
+    sent_u8 = g.empty_u8(4096, 0x5A)
+    sent_f = g.empty_f32(1024, -7.0)
+    sent_y = g.empty_u8(8192, 0xC3)
+    lst = [None if q == rank else sent_u8 for q in range(P)]
+    lsf = [None if q == rank else sent_f for q in range(P)]
+    B.echo_encode(st, sent_y, sent_u8, sent_f)
+    B.echo_call(st, sent_y, lst, lsf, lst, lsf, sent_u8, sent_f, sent_u8, sent_f, sent_y)
+    B.echo_call_plain(P, rank, sent_y, lst, lsf, lst, lsf, sent_u8, sent_f, sent_u8, sent_f, sent_y, 0)
+    B.echo_rs_call(st, sent_y, lst, lsf, sent_u8, sent_f, sent_y)
+    B.echo_update(st, sent_y, sent_u8, sent_f, sent_f)
+    B.echo_reduce_shard([sent_u8] * P, [sent_f] * P, sent_u8, sent_f, sent_y, sent_f, 0)
+    B.echo_reduce_shard_sum([sent_u8] * P, [sent_f] * P, sent_y, sent_f, 0)
+    B.echo_decode(sent_u8, sent_f, sent_y, 0, bits=8)
+    torch.cuda.synchronize()
+    assert (g.host(sent_u8, np.uint8) == 0x5A).all()
+    assert (g.host(sent_f, np.float32) == -7.0).all()
+    assert (g.host(sent_y, np.uint8) == 0xC3).all()
+
+
 @pytest.mark.parametrize("P,rank,k", [(1, 0, 3), (2, 1, 5), (3, 2, 4), (8, 0, 9), (8, 6, 33), (16, 9, 2)])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_call_plain_uncompensated(P, rank, k, bits):

@@ -691,3 +691,37 @@ def test_8bit_reduce_scatter_rank_mode():
     out = orc.rs_call(P, p, xs[p], mf0[p], ms0[p], recv_c, recv_s, bits=8)
     assert np.array_equal(out["y_own"], sim["y"][p * Cn:(p + 1) * Cn])
     assert np.array_equal(mf0[p], mf[p])
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_zero_padded_tail_stays_zero_and_padding_is_transparent(bits):
+    """A tensor that is not a whole number of groups per chunk is padded with
+    zeros by the caller.  Zero inputs give zero codes (the group maximum
+    ignores them), the P-way sum over them is zero, so the tail's outputs,
+    residuals and averages stay exactly zero call after call.  Chunk
+    ownership only decides which rank adds e2 to its residual, so on the
+    first call from zero state y on the real prefix, and the sum of the
+    ranks' averages, do not depend on how far the tensor was padded."""
+    P, real = 4, 1536 - 500
+    rng = np.random.default_rng(40 + bits)
+    runs = {}
+    for n in (1536, 3072):   # chunks of 384 and 768 elements: different owners
+        xs0 = [bf16_bits(rng.standard_normal(real) * (1 + p)) for p in range(P)] if n == 1536 else runs[1536]["x0"]
+        mf = [np.zeros(n, np.float32) for _ in range(P)]
+        ms = [np.zeros(n, np.float32) for _ in range(P)]
+        for call in range(3):
+            src = xs0 if call == 0 else [bf16_bits(rng.standard_normal(real)) for _ in range(P)]
+            xs = [np.concatenate([x, np.zeros(n - real, np.uint16)]) for x in src]
+            out = orc.simulate(xs, mf, ms, want_detail=True, bits=bits)
+            assert not out["y"][real:].any(), f"n={n} call {call}: y tail"
+            for p in range(P):
+                assert not mf[p][real:].view(np.uint32).any() and not ms[p][real:].view(np.uint32).any()
+                assert not out["r"][p][real:].view(np.uint32).any()
+                q = orc.unpack_codes(out["codes1"][p], n, bits)
+                assert not q[real:].any()
+            assert not orc.unpack_codes(out["codes2"], n, bits)[real:].any()
+            if call == 0:
+                first = dict(y=out["y"][:real].copy(), mf_sum=sum(m[:real].astype(np.float64) for m in mf))
+        runs[n] = dict(x0=xs0, **first)
+    assert np.array_equal(runs[1536]["y"], runs[3072]["y"])
+    np.testing.assert_allclose(runs[1536]["mf_sum"], runs[3072]["mf_sum"], rtol=0, atol=1e-6)
