@@ -361,6 +361,11 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
   const uint32_t nslices = (a.groups + 1u) >> 1;
 
   for (uint32_t s0 = wave * U; s0 < nslices; s0 += nwaves * U) {
+    // The own slot's index, opaque to the optimizer inside each step: left
+    // loop-invariant, its P comparisons are hoisted out of the loop and held
+    // as P live lane masks, which for large P spill the scalar registers.
+    int32_t own = a.rank;
+    asm volatile("" : "+s"(own));
     // issue every load of the U slices first
     bool ok[U];
     uint32_t g[U];
@@ -373,18 +378,23 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       ok[u] = (s0 + u < nslices) && (v < a.groups);
       g[u] = ok[u] ? v : 0u;
       const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
+      // A lane past the end reads group 0 (always present) and stores
+      // nothing, so the loads need no per-lane guard.  Only the own-slot test
+      // remains, and it is uniform: with a lane-varying guard per shard the
+      // compiler keeps one exec mask per shard, which for P > 9 no longer
+      // fits the scalar registers and spills into vector lanes.
 #pragma unroll
       for (int q = 0; q < P; ++q) {
         cw[u][q] = 0u;
         sc[u][q] = 0.f;
-        if (ok[u] && !(own_in_registers(MODE) && q == a.rank)) {
+        if (!(own_in_registers(MODE) && q == own)) {
           cw[u][q] = load_codes4<BITS>(a.codes[q], e);
           sc[u][q] = a.scales[q][g[u]];
         }
       }
       uint2 xw = make_uint2(0u, 0u);
       float4 f = make_float4(0.f, 0.f, 0.f, 0.f), s = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (own_in_registers(MODE) && ok[u]) {
+      if (own_in_registers(MODE)) {
         const u32x2 xv = ld_stream(reinterpret_cast<const u32x2*>(a.x + e));
         xw = make_uint2(xv.x, xv.y);
         if (own_reads_state(MODE)) {
@@ -412,8 +422,24 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
         m = halfwave_max(m);
         const float s1 = scale_of<BITS>(m);
         const float sd = code_divisor(s1);
+        int q1[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) d_own[k] = (float)quant_code<BITS>(xp[k], sd) * s1;
+        for (int k = 0; k < 4; ++k) {
+          q1[k] = quant_code<BITS>(xp[k], sd);
+          d_own[k] = (float)q1[k] * s1;
+        }
+        // the own slot holds the codes and scale it would have received, so
+        // the sum below decodes every slot alike (code * scale is d_own)
+        int32_t slot = own;
+        asm volatile("" : "+s"(slot));
+        const uint32_t own_word = pack_codes4<BITS>(q1);
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+          if (q == slot) {
+            cw[u][q] = own_word;
+            sc[u][q] = s1;
+          }
+        }
       }
 
       // S = d_0 + d_1 + ... + d_{P-1}, in rank order
@@ -422,9 +448,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
       for (int q = 0; q < P; ++q) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          float d;
-          if (own_in_registers(MODE) && q == a.rank) d = d_own[k];
-          else d = (float)code_at<BITS>(cw[u][q], k) * sc[u][q];
+          const float d = (float)code_at<BITS>(cw[u][q], k) * sc[u][q];
           S[k] = (q == 0) ? d : S[k] + d;
         }
       }

@@ -211,6 +211,46 @@ def test_call_rank_mode(P, rank, k, bits):
         case.check(want)
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_call_every_rank_count_and_slot(bits):
+    """Every P from 1 to 16 and every rank p < P (the own slot at every
+    position of the rank-order sum), an odd number of groups per chunk (a
+    half-empty last wave), two calls each: fused call and reduce-scatter call
+    against the oracle."""
+    g = gu()
+    for P in range(1, 17):
+        for rank in range(P):
+            k = 3
+            print(f"every-slot: P={P} rank={rank} bits={bits}", flush=True)
+            case = RankCase(P, rank, k, seed=1000 + 17 * P + rank, bits=bits)
+            for call in range(2):
+                x = x_of(case.n, 7 * call + 3 * P + rank)
+                case.gpu_call(g.dev(x))
+                case.check(case.oracle_call(x))
+            # uncompensated call: the own slot quantized from x alone
+            xp = x_of(case.n, 55 + P + rank)
+            B.echo_call_plain(P, rank, g.dev(xp), case.slot(case.recv_d, 0), case.slot(case.recv_d, 1),
+                              case.slot(case.gath_d, 0), case.slot(case.gath_d, 1), case.send_c,
+                              case.send_s, case.own_c, case.own_s, case.y, bits=bits)
+            want = orc.call(P, rank, xp, None, None, case.slot(case.recv, 0), case.slot(case.recv, 1),
+                            case.slot(case.gath, 0), case.slot(case.gath, 1), comp=False, bits=bits)
+            eq(g.host(case.own_c, np.uint8), want["own_codes2"], f"P={P} rank={rank} plain codes2")
+            eq(g.host(case.y, np.uint16), want["y"], f"P={P} rank={rank} plain y")
+            # reduce-scatter: the same own-slot position in its rank-order sum
+            mf, ms = state_of(case.n, P + rank, scale=0.1)
+            mfd, msd = g.dev(mf), g.dev(ms)
+            st = B.EchoState(mfd, msd, case.n, P, rank, bits=bits)
+            x = x_of(case.n, 99 + P + rank)
+            y_own = g.empty_bf16(case.Cn)
+            B.echo_rs_call(st, g.dev(x), case.slot(case.recv_d, 0), case.slot(case.recv_d, 1),
+                           case.send_c, case.send_s, y_own)
+            want = orc.rs_call(P, rank, x, mf, ms, case.slot(case.recv, 0), case.slot(case.recv, 1),
+                               bits=bits)
+            eq(g.host(y_own, np.uint16), want["y_own"], f"P={P} rank={rank} rs y_own")
+            eq(g.host(mfd, np.float32), mf, f"P={P} rank={rank} rs m_fast")
+            eq(g.host(msd, np.float32), ms, f"P={P} rank={rank} rs m_slow")
+
+
 @pytest.mark.parametrize("P,rank,k", [(8, 3, 5), (3, 1, 7), (1, 0, 2)])
 def test_phases_equal_fused_call_and_in_place(P, rank, k):
     g = gu()
