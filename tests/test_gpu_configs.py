@@ -242,6 +242,24 @@ def test_config_1gb_rank_mode():
     run.check_message_properties("call 22")
 
 
+@pytest.mark.timeout(900)
+def test_1gb_message_sixteen_ranks():
+    """The 1 GB message at the largest rank count (P = 16, rank 11): 15
+    incoming shards per chunk element, four calls with the averages carried,
+    windows of every chunk, the whole exit pass."""
+    P, rank, n = 16, 11, 1 << 29
+    say("1gb P=16: generating inputs")
+    x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 16, "x"), outlier_mult=20.0)
+    xd = g.dev(x)
+    run = RankRun(P, rank, n, seed=16, windows_per_chunk=2, label="1gb P=16")
+    for call in range(4):
+        run.call(xd)
+        run.check_windows(xd, f"call {call}")
+        say(f"1gb P=16: call {call} windows ok")
+    run.check_exit_full("call 3")
+    run.check_message_properties("call 3")
+
+
 @pytest.mark.parametrize("a", [1.0, 1.1])
 def test_deep_chain_on_the_gpu(a):
     """The deep chain h <- a h + y run through the GPU (P = 8 ranks simulated),
