@@ -300,6 +300,26 @@ WORKLOADS = {
 }
 
 
+def practical_ceiling(B, torch, stream, nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """The library's plain streaming copy (16 bytes per lane, non-temporal,
+    a grid covering the range) over nbytes: the bandwidth a kernel with no
+    arithmetic reaches on this GPU, read + write bytes per second."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        B.echo_stream_copy(src, dst, nbytes, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        B.echo_stream_copy(src, dst, nbytes, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"kernel": "echo_stream_copy (16 B per lane, non-temporal)", "bytes_per_launch": 2 * nbytes,
+            "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def calibration_copy(dev) -> None:
     """A plain device copy of known size (reads 1 GiB, writes 1 GiB): the
     reference that scales HBM counter readings to bytes."""
@@ -553,6 +573,7 @@ def main() -> int:
         "reduce": float(np.mean([e[1].elapsed_time(e[2]) for e in events])),
         "exit": float(np.mean([e[2].elapsed_time(e[3]) for e in events])),
     }
+    call_event_ms = [e[0].elapsed_time(e[3]) for e in events]
 
     # the fused entry point itself, same stream, for reference
     torch.cuda.synchronize()
@@ -561,6 +582,8 @@ def main() -> int:
         B.echo_call(st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, y, stream)
     torch.cuda.synchronize()
     call_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+
+    ceiling = practical_ceiling(B, torch, stream)
 
     bpe = bytes_per_element(P)
     entry_bytes = (N - C) * bpe["entry"]
@@ -585,6 +608,8 @@ def main() -> int:
         "pct_hbm_peak": round(100.0 * total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "algorithmic_bytes_per_step": int(total_bytes),
         "kernel_ms": {k: round(v, 4) for k, v in k_ms.items()},
+        "call_ms_events": {"mean": round(float(np.mean(call_event_ms)), 4),
+                           "median": round(float(np.median(call_event_ms)), 4)},
         "echo_call_ms": round(call_ms, 4),
         "roofline": {
             "kernel": "K_entry (k_stage1<entry>)",
@@ -598,6 +623,9 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    out["practical_ceiling"] = dict(
+        ceiling, entry_frac=round(achieved / ceiling["GBps"], 4),
+        call_frac=round(total_bytes / (ms_step * 1e-3) / 1e9 / ceiling["GBps"], 4))
     if not args.no_schedules:
         print("bench: critical-path schedules", file=sys.stderr, flush=True)
         e2 = torch.empty(C, dtype=torch.float32, device=dev)

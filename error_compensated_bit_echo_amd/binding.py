@@ -58,6 +58,7 @@ _SIGNATURES = {
     "echo_reduce_shard_sum": [C.c_int32, C.c_int64, C.c_int32, _pp, _pp, _vp, _vp, _vp],
     "echo_rs_reduce": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp],
     "echo_rs_call": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp, _vp, _vp],
+    "echo_stream_copy": [_vp, _vp, C.c_int64, _vp],
     "echo_get_config": [C.POINTER(EchoConfigC)],
     "echo_status_string": [C.c_int],
     "echo_version": [],
@@ -174,6 +175,14 @@ def echo_decode(codes, scales, y, n=None, stream=None, bits: int = 4) -> None:
         n = y.numel()
     _check(lib.echo_decode(int(n), int(bits), _ptr(codes), _ptr(scales), _ptr(y), _stream(stream)),
            "echo_decode")
+
+
+def echo_stream_copy(src, dst, nbytes=None, stream=None) -> None:
+    """Plain streaming copy (the bandwidth ceiling the kernels are measured
+    against); nbytes defaults to dst's size in bytes."""
+    if nbytes is None:
+        nbytes = dst.numel() * dst.element_size()
+    _check(lib.echo_stream_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)), "echo_stream_copy")
 
 
 def echo_update(st: EchoState, x, codes1, scales1, e2_own, stream=None) -> None:

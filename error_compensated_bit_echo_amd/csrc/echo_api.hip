@@ -761,4 +761,21 @@ const char* echo_status_string(int status) {
 
 int echo_version(void) { return ECHO_ABI_VERSION; }
 
+int echo_stream_copy(const void* src, void* dst, int64_t bytes, echo_stream_t stream) {
+  if (bytes < 0 || bytes % 16 != 0) return ECHO_ERR_SHAPE;
+  if (bytes == 0) return ECHO_SUCCESS;
+  if (!src || !dst) return ECHO_ERR_INVALID_ARGUMENT;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return ECHO_ERR_ALIGNMENT;
+  Aliases al;
+  al.out(dst, bytes);
+  al.in(src, bytes);
+  if (!al.ok()) return ECHO_ERR_ALIAS;
+  const int64_t n16 = bytes / 16;
+  int64_t blocks = (n16 + kBlock - 1) / kBlock;
+  if (blocks > (int64_t)kMaxBlocks) blocks = kMaxBlocks;
+  hipLaunchKernelGGL(k_copy16, dim3((uint32_t)blocks), dim3(kBlock), 0, (hipStream_t)stream,
+                     reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), n16);
+  return launch_status();
+}
+
 }  // extern "C"

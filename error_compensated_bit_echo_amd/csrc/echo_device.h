@@ -579,4 +579,11 @@ __global__ __launch_bounds__(kBlock) void k_zero2(float4* a, float4* b, int64_t 
   }
 }
 
+// a plain streaming copy, 16 bytes per lane (the practical bandwidth ceiling)
+__global__ __launch_bounds__(kBlock) void k_copy16(const u32x4* src, u32x4* dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += stride)
+    st_stream(dst + i, ld_stream(src + i));
+}
+
 }  // namespace echo

@@ -259,6 +259,15 @@ int echo_rs_call(const echo_state* st, const uint16_t* x, const uint8_t* const* 
                  const float* const* recv_scales, uint8_t* send_codes, float* send_scales,
                  uint16_t* y_own, echo_stream_t stream);
 
+/* ---- measurement ------------------------------------------------------------
+ * A plain streaming copy with the launch shape and cache hints of the path's
+ * kernels (one 16-byte vector per lane, a grid covering the range,
+ * non-temporal loads and stores): the practical HBM ceiling the kernels are
+ * measured against.  Not part of the method.  bytes % 16 == 0 and both
+ * pointers 16-byte aligned (ECHO_ERR_SHAPE / ECHO_ERR_ALIGNMENT); the ranges
+ * may not overlap (ECHO_ERR_ALIAS); bytes == 0 is a no-op. */
+int echo_stream_copy(const void* src, void* dst, int64_t bytes, echo_stream_t stream);
+
 /* ---- misc ------------------------------------------------------------------ */
 int echo_get_config(echo_config* out);      /* the named parameters above */
 const char* echo_status_string(int status); /* static string, never NULL */

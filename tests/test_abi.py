@@ -26,7 +26,7 @@ def test_header_declares_the_calls():
     for want in ("echo_state_init", "echo_encode", "echo_reduce_shard", "echo_decode",
                  "echo_update", "echo_call", "echo_call_entry", "echo_call_reduce",
                  "echo_call_exit", "echo_call_plain", "echo_reduce_shard_sum", "echo_rs_reduce",
-                 "echo_rs_call", "echo_get_config", "echo_status_string",
+                 "echo_rs_call", "echo_stream_copy", "echo_get_config", "echo_status_string",
                  "echo_version"):
         assert want in names
 
@@ -229,6 +229,15 @@ def test_empty_calls_are_noops():
     assert rc(B.echo_decode, None, None, None, -128) == -2
     assert rc(B.echo_reduce_shard, nulls * 3, nulls * 3, None, None, None, None, 0) == -4
     assert rc(B.echo_reduce_shard_sum, nulls, nulls, None, None, 0, bits=2) == -7
+
+
+def test_stream_copy_rejections():
+    assert rc(B.echo_stream_copy, 3 * A, 4 * A, 100) == -2
+    assert rc(B.echo_stream_copy, 3 * A, 4 * A, -16) == -2
+    assert rc(B.echo_stream_copy, None, 4 * A, 256) == -1
+    assert rc(B.echo_stream_copy, 3 * A + 8, 4 * A, 256) == -3
+    assert rc(B.echo_stream_copy, 3 * A, 3 * A + 128, 256) == -6
+    B.echo_stream_copy(None, None, 0, stream=0)  # empty: a no-op
 
 
 def test_build_entry_check_matches_header():

@@ -798,3 +798,15 @@ def test_prepared_call_matches_echo_call():
         eq(g.host(b.y, np.uint16), g.host(a.y, np.uint16), f"call {call} y")
         eq(g.host(b.mfd, np.float32), g.host(a.mfd, np.float32), f"call {call} m_fast")
         eq(g.host(b.own_c, np.uint8), g.host(a.own_c, np.uint8), f"call {call} codes2")
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 257 + 16 * 256 * 3, (1 << 20) + 48])
+def test_stream_copy_copies_exactly(nbytes):
+    """The measurement copy moves every byte and touches nothing beyond."""
+    g = gu()
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=g.DEV)
+    dst = g.empty_u8(nbytes + 64, 0xEE)
+    B.echo_stream_copy(src, dst, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert (g.host(dst[nbytes:], np.uint8) == 0xEE).all()
