@@ -503,7 +503,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures the per-rank pipeline on one GPU; this build has no "
+        print("bench.py measures the per-rank pipeline on one GPU; the library has no "
               "multi-GPU transport, so --gpus must be 1", file=sys.stderr)
         return 2
     if args.workload != "1gb":
