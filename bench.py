@@ -139,8 +139,8 @@ def cpu_baseline(x, recv, gath, P: int, rank: int, n_sample: int, calls: int):
 
 def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, y, e2,
               N, P, rank, steps):
-    """The compensation's cost on the critical path (the pages' schedule runs
-    the averages' update beside the next matrix multiplication).  Times, per
+    """The compensation's cost on the critical path (in the pages' schedule
+    the averages' update overlaps the following matrix multiplication).  Times, per
     call: the fused call; the uncompensated call; the split schedule's
     critical path (entry pass with the averages read-only, reduce, exit)
     with the update on a side stream; and each followed by a matmul that

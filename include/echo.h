@@ -3,13 +3,14 @@
  * error-compensated 4-bit all-reduce on one AMD Instinct MI355X (gfx950).
  *
  * Method: "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication for
- * LLM Training and Inference" (arXiv 2610.14277v1).  The all-reduce moves
- * 4-bit integers and sums in high precision, so every value is quantized at
- * most twice per call ("Echo: Error-Compensated 4-Bit Tensor-Parallel
- * Communication", Abstract); a correction built from two moving averages
- * with different decay rates is added to the input before each all-reduce,
- * and the averages are refreshed from the output residual ("Tensor-parallel
- * traffic drops to 4 bits", Interpretation).
+ * LLM Training and Inference" (arXiv 2610.14277v1).  The all-reduce carries
+ * 4-bit integer codes, accumulates them in a wider floating-point format and
+ * passes no value through the quantizer more than two times per call,
+ * whatever the rank count ("Echo: Error-Compensated 4-Bit Tensor-Parallel
+ * Communication", Abstract).  Before each all-reduce the input is shifted by
+ * a correction formed from a fast-decaying and a slow-decaying average of
+ * earlier injected error; afterwards both averages absorb the error the call
+ * injected ("Tensor-parallel traffic drops to 4 bits", Interpretation).
  *
  * One rank's view.  P ranks each hold an n-element bf16 tensor.  Chunk j is
  * the element range [j*n/P, (j+1)*n/P); rank j owns chunk j.  A call is:
@@ -142,8 +143,9 @@ int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* 
                 echo_stream_t stream);
 
 /* Reduce stage for one chunk of chunk_n elements ("Echo: Error-Compensated
- * 4-Bit Tensor-Parallel Communication", Abstract: 4-bit transport,
- * high-precision sum, quantized at most twice): shard_codes /
+ * 4-Bit Tensor-Parallel Communication", Abstract: the 4-bit codes are summed
+ * in a wide format and requantized once more, the last quantization a value
+ * sees): shard_codes /
  * shard_scales are host arrays of nranks device pointers (shard q = rank q's
  * stage-1 message of this chunk: codes[chunk_n/2], scales[chunk_n/128]).
  * S = d_0 + d_1 + ... + d_{P-1} in binary32, in that order (d = code*scale);
@@ -210,7 +212,7 @@ int echo_call(const echo_state* st, const uint16_t* x, const uint8_t* const* rec
               uint8_t* own_codes2, float* own_scales2, uint16_t* y, echo_stream_t stream);
 
 /* The uncompensated 4-bit all-reduce compute path: the same three phases with
- * x' = f32(x) and no averages (the pages' "uncompensated 4-bit all-reduce",
+ * x' = f32(x) and no averages (the pages' uncompensated 4-bit control,
  * "Tensor-parallel traffic drops to 4 bits", Interpretation).  Arguments as
  * echo_call, with the rank geometry given directly.  Also the control of the
  * deep-chain experiment, and the critical path the compensation is measured
@@ -221,8 +223,8 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, int32_t bits, const
                     uint8_t* send_codes, float* send_scales, uint8_t* own_codes2,
                     float* own_scales2, uint16_t* y, echo_stream_t stream);
 
-/* Deferred update.  The pages run the averages' update beside the next matrix
- * multiplication, off the critical path ("Tensor-parallel traffic drops to 4
+/* Deferred update.  In the pages' schedule the averages' update overlaps the
+ * following matrix multiplication, off the critical path ("Tensor-parallel traffic drops to 4
  * bits", Interpretation).  With this API that schedule is: echo_encode (the
  * whole tensor, averages read-only; chunk p of its output is the own stage-1
  * message) -> transport -> echo_reduce_shard (slot p = that own message, out_e2
@@ -232,8 +234,8 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, int32_t bits, const
  * echo_call. */
 
 /* ---- reduce-scatter only (sequence parallelism) ------------------------------
- * The pages name the reduce-scatter of sequence parallelism as a natural next
- * target ("Tensor-parallel traffic drops to 4 bits", Perspective).  Reading:
+ * The pages propose the reduce-scatter of sequence parallelism as a further
+ * use ("Tensor-parallel traffic drops to 4 bits", Perspective).  Reading:
  * the entry pass is the all-reduce's; rank p sums the P stage-1 shards of its
  * chunk in binary32, rank order, and outputs the sum as bf16 (round to nearest
  * even) -- there is no second quantization, each value is quantized once; the

@@ -10,15 +10,17 @@
  * "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication" (EC),
  * "Tensor-parallel traffic drops to 4 bits" (TP), "How Echo lets big AI
  * models train faster" (HE).
- *   - the all-reduce payload travels as 4-bit integers and is summed in
- *     high precision (TP, Interpretation; EC, Abstract);
- *   - each value is quantized at most twice per call for any number of GPUs
- *     (EC, Abstract; HE, "How Echo keeps errors from snowballing");
- *   - a correction built from two moving averages with different decay
- *     rates is added to the input before each all-reduce, and the averages
- *     are refreshed from the output residual (TP, Interpretation);
- *   - the sum reveals the error the call injected and feeding it back makes
- *     old errors cancel (EC, Abstract).
+ *   - the payload crosses the interconnect as 4-bit integer codes and is
+ *     accumulated in a wider floating-point format (TP, Interpretation; EC,
+ *     Abstract);
+ *   - no value is quantized more than two times in a call, whatever the
+ *     rank count (EC, Abstract; HE, "How Echo keeps errors from snowballing");
+ *   - before each all-reduce the input is shifted by a correction formed
+ *     from a fast- and a slow-decaying average of past injected error, and
+ *     the averages then absorb the error that call injected (TP,
+ *     Interpretation);
+ *   - forming the sum exposes the injected error, and folding it into later
+ *     calls lets earlier errors cancel out (EC, Abstract).
  * Every detail the pages leave open (group size, scale type, code range,
  * rounding, nibble order, decays, how the averages combine, the residual's
  * exact definition) follows the stated readings: see echo_oracle.h.

@@ -37,7 +37,7 @@ extern "C" {
 #define ORC_QMAX8 127        /* 8-bit promotion of a call: codes in [-127, 127] */
 
 /* Number of values the quantizer has processed, per stage (1 = entry,
- * 2 = reduce).  Used by the "quantized at most twice" pin. */
+ * 2 = reduce).  Used by the pin on the number of quantizations per value. */
 void orc_counters_reset(void);
 long long orc_counter(int stage);
 

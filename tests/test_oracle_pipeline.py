@@ -3,12 +3,12 @@
 Pages: "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication" (EC),
 "Tensor-parallel traffic drops to 4 bits" (TP), "How Echo lets big AI models
 train faster" (HE).  What they fix and how each is checked:
-  * each value is quantized at most twice per call for any number of GPUs
-    (EC, Abstract; HE, "How Echo keeps errors from snowballing"):
+  * no value is quantized more than two times in a call, whatever the rank
+    count (EC, Abstract; HE, "How Echo keeps errors from snowballing"):
     instrumented counts, and a ring all-reduce that requantizes at every
     hop as the contrast whose error grows with P;
-  * the sum is formed in high precision and reveals the injected error,
-    which is fed back (TP, Interpretation; EC, Abstract): the residual
+  * the sum is accumulated in a wide format, which exposes the injected
+    error so that it can be fed back (TP, Interpretation; EC, Abstract): the residual
     identity sum_p r_p = y - sum_p x'_p;
   * the accumulated error stays bounded independently of depth (EC,
     Abstract; TP, Perspective): the deep-chain test, compensated vs
