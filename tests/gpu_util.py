@@ -105,4 +105,4 @@ def gpu_simulate_call(ranks, xs_np):
     return codes2, scales2, own2, own2s
 
 
-from windows import WindowOracle, pick_windows  # noqa: E402,F401
+from windows import RSWindowOracle, WindowOracle, pick_windows  # noqa: E402,F401

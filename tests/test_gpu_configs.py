@@ -78,29 +78,32 @@ def test_config_decode_full_simulation():
 class RankRun:
     """Device buffers of one rank-mode sequence plus the oracle's windows."""
 
-    def __init__(self, P, rank, n, seed, windows_per_chunk=2, W=4, label=""):
+    def __init__(self, P, rank, n, seed, windows_per_chunk=2, W=4, label="", bits=4):
         self.P, self.rank, self.n, self.C = P, rank, n, n // P
         self.label = label
+        self.bits = bits
+        self.f = 1 if bits == 8 else 2  # elements per code byte
         C = self.C
         self.recv = [None if q == rank else I.int4_message(C, I.stream_key(label, seed, "recv", q),
-                                                           zero_group_frac=1e-3)
+                                                           zero_group_frac=1e-3, bits=bits)
                      for q in range(P)]
         self.gath = [None if j == rank else
                      I.int4_message(C, I.stream_key(label, seed, "gath", j), scale_lo=0.15,
-                                    scale_hi=1.5, zero_group_frac=1e-3)
+                                    scale_hi=1.5, zero_group_frac=1e-3, bits=bits)
                      for j in range(P)]
         self.recv_d = [None if m is None else (g.dev(m[0]), g.dev(m[1])) for m in self.recv]
         self.gath_d = [None if m is None else (g.dev(m[0]), g.dev(m[1])) for m in self.gath]
         self.mf = g.empty_f32(n)
         self.ms = g.empty_f32(n)
         self.st = B.echo_state_init(self.mf, self.ms, n, P, rank)
-        self.send_c = g.empty_u8(n // 2)
+        self.st.bits = bits
+        self.send_c = g.empty_u8(n // self.f)
         self.send_s = g.empty_f32(n // 128)
-        self.own_c = g.empty_u8(C // 2)
+        self.own_c = g.empty_u8(C // self.f)
         self.own_s = g.empty_f32(C // 128)
         self.y = g.empty_bf16(n)
         rng = np.random.default_rng(seed)
-        self.wins = [g.WindowOracle(P, rank, j, off, W)
+        self.wins = [g.WindowOracle(P, rank, j, off, W, bits=bits)
                      for j, off in g.pick_windows(P, C, W, rng, windows_per_chunk)]
 
     def call(self, xd):
@@ -117,23 +120,23 @@ class RankRun:
             ce = w.chunk_elems()
             x_win = g.host(xd[es], np.uint16)
             if w.j == r:
-                msg = [None if q == r else (self.recv[q][0][ce.start // 2:ce.stop // 2],
+                msg = [None if q == r else (self.recv[q][0][w.code_slice(ce)],
                                             self.recv[q][1][ce.start // 128:ce.stop // 128])
                        for q in range(self.P)]
             else:
                 m = self.gath[w.j]
-                msg = (m[0][ce.start // 2:ce.stop // 2], m[1][ce.start // 128:ce.stop // 128])
+                msg = (m[0][w.code_slice(ce)], m[1][ce.start // 128:ce.stop // 128])
             want = w.call(x_win, msg)
             what = f"{self.label} {tag} window (chunk {w.j}, group {w.off})"
             g.eq(g.host(self.y[es], np.uint16), want["y"], what + " y")
             g.eq(g.host(self.mf[es], np.float32), want["m_fast"], what + " m_fast")
             g.eq(g.host(self.ms[es], np.float32), want["m_slow"], what + " m_slow")
             if w.j == r:
-                g.eq(g.host(self.own_c[ce.start // 2:ce.stop // 2], np.uint8), want["codes"], what + " codes2")
+                g.eq(g.host(self.own_c[w.code_slice(ce)], np.uint8), want["codes"], what + " codes2")
                 g.eq(g.host(self.own_s[ce.start // 128:ce.stop // 128], np.float32), want["scales"],
                      what + " scales2")
             else:
-                g.eq(g.host(self.send_c[es.start // 2:es.stop // 2], np.uint8), want["codes"], what + " send codes")
+                g.eq(g.host(self.send_c[w.code_slice(es)], np.uint8), want["codes"], what + " send codes")
                 g.eq(g.host(self.send_s[es.start // 128:es.stop // 128], np.float32), want["scales"],
                      what + " send scales")
 
@@ -145,8 +148,9 @@ class RankRun:
         C, r = self.C, self.rank
         y = g.host(self.y, np.uint16)
         for j in range(self.P):
-            want = (orc.decode(g.host(self.own_c, np.uint8), g.host(self.own_s, np.float32), C)
-                    if j == r else orc.decode(self.gath[j][0], self.gath[j][1], C))
+            want = (orc.decode(g.host(self.own_c, np.uint8), g.host(self.own_s, np.float32), C,
+                               bits=self.bits)
+                    if j == r else orc.decode(self.gath[j][0], self.gath[j][1], C, bits=self.bits))
             g.eq(y[j * C:(j + 1) * C], want, f"{self.label} {tag} y chunk {j}")
 
     def check_message_properties(self, tag):
@@ -156,13 +160,17 @@ class RankRun:
         C, r = self.C, self.rank
         sc = g.host(self.send_c, np.uint8)
         ss = g.host(self.send_s, np.float32)
-        keep = np.ones(self.n // 2, bool)
-        keep[r * C // 2:(r + 1) * C // 2] = False
+        f = self.f
+        keep = np.ones(self.n // f, bool)
+        keep[r * C // f:(r + 1) * C // f] = False
         keep_s = np.ones(self.n // 128, bool)
         keep_s[r * C // 128:(r + 1) * C // 128] = False
         for codes, scales in ((sc[keep], ss[keep_s]),
                               (g.host(self.own_c, np.uint8), g.host(self.own_s, np.float32))):
-            assert not np.any((codes & 0xF) == 8) and not np.any((codes >> 4) == 8), tag
+            if self.bits == 8:
+                assert not np.any(codes == 0x80), tag
+            else:
+                assert not np.any((codes & 0xF) == 8) and not np.any((codes >> 4) == 8), tag
             assert np.all(np.isfinite(scales)) and np.all(scales >= 0), tag
 
 
@@ -258,6 +266,63 @@ def test_1gb_message_sixteen_ranks():
         say(f"1gb P=16: call {call} windows ok")
     run.check_exit_full("call 3")
     run.check_message_properties("call 3")
+
+
+@pytest.mark.timeout(900)
+def test_1gb_message_8bit_promoted_call():
+    """The 1 GB message with 8-bit codes (the promoted width), as the bench
+    times it: P = 8, rank 0, four calls with the averages carried, windows
+    of every chunk, the whole exit pass, no -128 code in any message."""
+    P, rank, n = 8, 0, 1 << 29
+    say("1gb 8-bit: generating inputs")
+    x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 8, "x"), outlier_mult=20.0)
+    xd = g.dev(x)
+    run = RankRun(P, rank, n, seed=8, windows_per_chunk=2, label="1gb 8-bit", bits=8)
+    for call in range(4):
+        run.call(xd)
+        run.check_windows(xd, f"call {call}")
+        say(f"1gb 8-bit: call {call} windows ok")
+    run.check_exit_full("call 3")
+    run.check_message_properties("call 3")
+
+
+@pytest.mark.timeout(900)
+def test_1gb_message_reduce_scatter():
+    """The reduce-scatter call at the bench's size (bf16[2^29], P = 8, rank
+    0): four calls with the averages carried, windows of every chunk (send
+    codes or y_own, and the averages) against the oracle."""
+    P, rank, n = 8, 0, 1 << 29
+    C = n // P
+    say("1gb reduce-scatter: generating inputs")
+    x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 0, "x"), outlier_mult=20.0)
+    xd = g.dev(x)
+    recv = [None if q == rank else I.int4_message(C, I.stream_key("1gb rs", q), zero_group_frac=1e-3)
+            for q in range(P)]
+    rc = [None if m is None else g.dev(m[0]) for m in recv]
+    rs = [None if m is None else g.dev(m[1]) for m in recv]
+    mf, ms = g.empty_f32(n), g.empty_f32(n)
+    st = B.echo_state_init(mf, ms, n, P, rank)
+    send_c, send_s, y_own = g.empty_u8(n // 2), g.empty_f32(n // 128), g.empty_bf16(C)
+    rng = np.random.default_rng(12)
+    wins = [g.RSWindowOracle(P, rank, j, off, 4) for j, off in g.pick_windows(P, C, 4, rng, 2)]
+    for call in range(4):
+        B.echo_rs_call(st, xd, rc, rs, send_c, send_s, y_own)
+        torch.cuda.synchronize()
+        for w in wins:
+            es, ce = w.elems(C), w.chunk_elems()
+            msg = ([None if q == rank else (recv[q][0][w.code_slice(ce)], recv[q][1][ce.start // 128:ce.stop // 128])
+                    for q in range(P)] if w.j == rank else None)
+            want = w.call(g.host(xd[es], np.uint16), msg)
+            what = f"1gb rs call {call} window (chunk {w.j}, group {w.off})"
+            g.eq(g.host(mf[es], np.float32), want["m_fast"], what + " m_fast")
+            g.eq(g.host(ms[es], np.float32), want["m_slow"], what + " m_slow")
+            if w.j == rank:
+                g.eq(g.host(y_own[ce], np.uint16), want["y_own"], what + " y_own")
+            else:
+                g.eq(g.host(send_c[w.code_slice(es)], np.uint8), want["codes"], what + " send codes")
+                g.eq(g.host(send_s[es.start // 128:es.stop // 128], np.float32), want["scales"],
+                     what + " send scales")
+        say(f"1gb reduce-scatter: call {call} windows ok")
 
 
 @pytest.mark.parametrize("a", [1.0, 1.1])

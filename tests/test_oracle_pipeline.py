@@ -357,7 +357,8 @@ def test_deep_chain_compensated_bounded_uncompensated_grows():
     assert ratio_off[L] > 8.0  # ~ sqrt(256) = 16 for independent errors
 
 
-def test_windows_of_a_rank_mode_sequence_match_the_full_run():
+@pytest.mark.parametrize("bits", [4, 8])
+def test_windows_of_a_rank_mode_sequence_match_the_full_run(bits):
     """Group locality: every output of a group depends only on that group's
     inputs, so a window embedded in a small rank-mode problem and carried
     through a call sequence reproduces the full problem's window exactly (the
@@ -368,31 +369,65 @@ def test_windows_of_a_rank_mode_sequence_match_the_full_run():
     P, rank, k = 8, 3, 7
     n = P * G * k
     Cn = n // P
-    recv = [None if q == rank else I.int4_message(Cn, I.stream_key("loc", q), zero_group_frac=0.05)
+    recv = [None if q == rank else I.int4_message(Cn, I.stream_key("loc", q), zero_group_frac=0.05,
+                                                  bits=bits)
             for q in range(P)]
-    gath = [None if j == rank else I.int4_message(Cn, I.stream_key("locg", j)) for j in range(P)]
+    gath = [None if j == rank else I.int4_message(Cn, I.stream_key("locg", j), bits=bits)
+            for j in range(P)]
     mf = np.zeros(n, np.float32)
     ms = np.zeros(n, np.float32)
     rng = np.random.default_rng(5)
-    wins = [WindowOracle(P, rank, j, off, 2) for j, off in pick_windows(P, Cn, 2, rng, 2)]
+    wins = [WindowOracle(P, rank, j, off, 2, bits=bits) for j, off in pick_windows(P, Cn, 2, rng, 2)]
     for call in range(6):
         x = bf16_bits(rng.standard_normal(n) * (1 + call))
         out = orc.call(P, rank, x, mf, ms, [m and m[0] for m in recv], [m and m[1] for m in recv],
-                       [m and m[0] for m in gath], [m and m[1] for m in gath])
+                       [m and m[0] for m in gath], [m and m[1] for m in gath], bits=bits)
         for w in wins:
             es, ce = w.elems(Cn), w.chunk_elems()
             if w.j == rank:
-                msg = [None if q == rank else (recv[q][0][ce.start // 2:ce.stop // 2],
+                msg = [None if q == rank else (recv[q][0][w.code_slice(ce)],
                                                recv[q][1][ce.start // G:ce.stop // G]) for q in range(P)]
             else:
-                msg = (gath[w.j][0][ce.start // 2:ce.stop // 2], gath[w.j][1][ce.start // G:ce.stop // G])
+                msg = (gath[w.j][0][w.code_slice(ce)], gath[w.j][1][ce.start // G:ce.stop // G])
             want = w.call(x[es], msg)
             assert np.array_equal(out["y"][es], want["y"])
             assert np.array_equal(mf[es], want["m_fast"]) and np.array_equal(ms[es], want["m_slow"])
             if w.j == rank:
-                assert np.array_equal(out["own_codes2"][ce.start // 2:ce.stop // 2], want["codes"])
+                assert np.array_equal(out["own_codes2"][w.code_slice(ce)], want["codes"])
             else:
-                assert np.array_equal(out["send_codes"][es.start // 2:es.stop // 2], want["codes"])
+                assert np.array_equal(out["send_codes"][w.code_slice(es)], want["codes"])
+                assert np.array_equal(out["send_scales"][es.start // G:es.stop // G], want["scales"])
+
+
+def test_reduce_scatter_windows_match_the_full_run():
+    """The locality argument for the reduce-scatter call: windows embedded in
+    small problems reproduce the full problem's send codes, y_own and
+    averages over a call sequence."""
+    from error_compensated_bit_echo_amd import inputs as I
+    from windows import RSWindowOracle, pick_windows
+
+    P, rank, k = 4, 2, 5
+    n = P * G * k
+    Cn = n // P
+    recv = [None if q == rank else I.int4_message(Cn, I.stream_key("rsloc", q), zero_group_frac=0.05)
+            for q in range(P)]
+    mf = np.zeros(n, np.float32)
+    ms = np.zeros(n, np.float32)
+    rng = np.random.default_rng(6)
+    wins = [RSWindowOracle(P, rank, j, off, 2) for j, off in pick_windows(P, Cn, 2, rng, 2)]
+    for call in range(5):
+        x = bf16_bits(rng.standard_normal(n) * (1 + call))
+        out = orc.rs_call(P, rank, x, mf, ms, [m and m[0] for m in recv], [m and m[1] for m in recv])
+        for w in wins:
+            es, ce = w.elems(Cn), w.chunk_elems()
+            msg = [None if q == rank else (recv[q][0][w.code_slice(ce)], recv[q][1][ce.start // G:ce.stop // G])
+                   for q in range(P)] if w.j == rank else None
+            want = w.call(x[es], msg)
+            assert np.array_equal(mf[es], want["m_fast"]) and np.array_equal(ms[es], want["m_slow"])
+            if w.j == rank:
+                assert np.array_equal(out["y_own"][ce], want["y_own"])
+            else:
+                assert np.array_equal(out["send_codes"][w.code_slice(es)], want["codes"])
                 assert np.array_equal(out["send_scales"][es.start // G:es.stop // G], want["scales"])
 
 
