@@ -78,7 +78,7 @@ def test_config_decode_full_simulation():
 class RankRun:
     """Device buffers of one rank-mode sequence plus the oracle's windows."""
 
-    def __init__(self, P, rank, n, seed, windows_per_chunk=2, W=4, label="", bits=4):
+    def __init__(self, P, rank, n, seed, windows_per_chunk=2, W=4, label="", bits=4, comp=True):
         self.P, self.rank, self.n, self.C = P, rank, n, n // P
         self.label = label
         self.bits = bits
@@ -103,13 +103,36 @@ class RankRun:
         self.own_s = g.empty_f32(C // 128)
         self.y = g.empty_bf16(n)
         rng = np.random.default_rng(seed)
-        self.wins = [g.WindowOracle(P, rank, j, off, W, bits=bits)
+        self.wins = [g.WindowOracle(P, rank, j, off, W, bits=bits, comp=comp)
                      for j, off in g.pick_windows(P, C, W, rng, windows_per_chunk)]
 
     def call(self, xd):
         sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
         B.echo_call(self.st, xd, sl(self.recv_d, 0), sl(self.recv_d, 1), sl(self.gath_d, 0),
                     sl(self.gath_d, 1), self.send_c, self.send_s, self.own_c, self.own_s, self.y)
+
+    def call_plain(self, xd):
+        sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
+        B.echo_call_plain(self.P, self.rank, xd, sl(self.recv_d, 0), sl(self.recv_d, 1),
+                          sl(self.gath_d, 0), sl(self.gath_d, 1), self.send_c, self.send_s,
+                          self.own_c, self.own_s, self.y, bits=self.bits)
+
+    def call_split(self, xd, e2, side):
+        """The pages' schedule: the critical path (entry pass with the
+        averages read-only, reduce of the own chunk with e2 kept, exit) on
+        the current stream, then the update on a side stream."""
+        P, r, C, f = self.P, self.rank, self.C, self.f
+        main = torch.cuda.current_stream()
+        sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
+        sh_c = [self.send_c[r * C // f:(r + 1) * C // f] if q == r else self.recv_d[q][0] for q in range(P)]
+        sh_s = [self.send_s[r * C // 128:(r + 1) * C // 128] if q == r else self.recv_d[q][1] for q in range(P)]
+        B.echo_encode(self.st, xd, self.send_c, self.send_s, main)
+        B.echo_reduce_shard(sh_c, sh_s, self.own_c, self.own_s, self.y[r * C:(r + 1) * C], e2, chunk_n=C,
+                            stream=main, bits=self.bits)
+        B.echo_call_exit(self.st, sl(self.gath_d, 0), sl(self.gath_d, 1), self.y, main)
+        side.wait_stream(main)
+        B.echo_update(self.st, xd, self.send_c, self.send_s, e2, side)
+        main.wait_stream(side)
 
     def check_windows(self, xd, tag):
         """Run every window's oracle one call further and compare."""
@@ -323,6 +346,30 @@ def test_1gb_message_reduce_scatter():
                 g.eq(g.host(send_s[es.start // 128:es.stop // 128], np.float32), want["scales"],
                      what + " send scales")
         say(f"1gb reduce-scatter: call {call} windows ok")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("schedule", ["uncompensated", "split"])
+def test_1gb_message_other_schedules(schedule):
+    """The bench's other 1 GB schedules: the uncompensated call, and the
+    split schedule (averages read-only on the critical path, the update on a
+    side stream); four calls, windows of every chunk against the oracle."""
+    P, rank, n = 8, 0, 1 << 29
+    say(f"1gb {schedule}: generating inputs")
+    x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 0, "x"), outlier_mult=20.0)
+    xd = g.dev(x)
+    run = RankRun(P, rank, n, seed=21, windows_per_chunk=2, label=f"1gb {schedule}",
+                  comp=schedule != "uncompensated")
+    e2 = g.empty_f32(n // P)
+    side = torch.cuda.Stream()
+    for call in range(4):
+        if schedule == "uncompensated":
+            run.call_plain(xd)
+        else:
+            run.call_split(xd, e2, side)
+        run.check_windows(xd, f"call {call}")
+        say(f"1gb {schedule}: call {call} windows ok")
+    run.check_exit_full("call 3")
 
 
 @pytest.mark.parametrize("a", [1.0, 1.1])

@@ -13,12 +13,13 @@ class WindowOracle:
     window's inputs (the other chunks zero) computes exactly the window's
     outputs; its chunk-j averages are carried from call to call."""
 
-    def __init__(self, P, rank, j, off, W, mf0=None, ms0=None, bits=4):
+    def __init__(self, P, rank, j, off, W, mf0=None, ms0=None, bits=4, comp=True):
         from oracle import oracle as orc
 
         self.orc = orc
         self.P, self.rank, self.j, self.off, self.W = P, rank, j, off, W
         self.bits = bits
+        self.comp = comp  # False: the uncompensated call (the averages stay zero)
         self.Cm = W * 128
         self.cbm = self.Cm if bits == 8 else self.Cm // 2  # code bytes of the window
         self.nm = P * self.Cm
@@ -56,7 +57,8 @@ class WindowOracle:
         recv_s = [None if q == r else (msg_win[q][1] if j == r else zs) for q in range(P)]
         gath_c = [None if q == r else (msg_win[0] if q == j else zc) for q in range(P)]
         gath_s = [None if q == r else (msg_win[1] if q == j else zs) for q in range(P)]
-        out = self.orc.call(P, r, x, self.mf, self.ms, recv_c, recv_s, gath_c, gath_s, bits=self.bits)
+        out = self.orc.call(P, r, x, self.mf, self.ms, recv_c, recv_s, gath_c, gath_s, comp=self.comp,
+                            bits=self.bits)
         cs = slice(j * self.cbm, (j + 1) * self.cbm)
         gs = slice(j * Cm // 128, (j + 1) * Cm // 128)
         es = slice(j * Cm, (j + 1) * Cm)
