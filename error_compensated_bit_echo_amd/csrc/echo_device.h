@@ -1,7 +1,7 @@
 // echo_device.h -- gfx950 device code of libecho: the Echo rank pipeline
 // (arXiv 2610.14277v1; "Tensor-parallel traffic drops to 4 bits", Interpretation, for
 // the compensator; "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication", Abstract, for the 4-bit
-// transport with a high-precision sum).
+// transport whose codes are summed in binary32).
 //
 // Work layout.  Every kernel walks 128-element quantization groups.  The
 // stage-1 / reduce kernels give each 64-lane wavefront a "slice" of two
