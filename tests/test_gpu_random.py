@@ -1,0 +1,82 @@
+"""Seeded random sweep of the GPU path against the oracle: drawn rank counts,
+ranks, chunk lengths (1 to 40 groups: every parity of the last wave's slice),
+code widths, input magnitudes and entry points (fused call, in place, the
+phased calls, the uncompensated call, the reduce-scatter call), two calls
+each with the averages carried.  Bit-exact."""
+import numpy as np
+import pytest
+
+import gpu_util as g
+from error_compensated_bit_echo_amd import binding as B
+from error_compensated_bit_echo_amd import inputs as I
+from oracle import oracle as orc
+from test_gpu_parity import RankCase, eq
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("call", "in_place", "phased", "plain", "rs")
+
+
+def _cases(count=300, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        P = int(rng.integers(1, 17))
+        out.append(dict(i=i, P=P, rank=int(rng.integers(0, P)), k=int(rng.integers(1, 41)),
+                        bits=int(rng.choice([4, 8])), mode=MODES[i % len(MODES)],
+                        log2_scale=int(rng.integers(-12, 13))))
+    return out
+
+
+def _x(n, case, call):
+    v = I.normal(n, I.stream_key("random-sweep", case["i"], call)) * 2.0 ** case["log2_scale"]
+    v[: n // 7] *= 0.0 if case["i"] % 3 == 0 else 1.0  # some cases start with all-zero groups
+    return I.to_bf16_bits(v)
+
+
+@pytest.mark.timeout(600)
+def test_random_sweep_bit_exact():
+    for case in _cases():
+        P, rank, k, bits, mode = case["P"], case["rank"], case["k"], case["bits"], case["mode"]
+        print(f"random sweep: case {case}", flush=True)
+        rc = RankCase(P, rank, k, seed=5000 + case["i"], bits=bits)
+        what = f"case {case['i']} ({mode}, P={P}, rank={rank}, k={k}, bits={bits})"
+        for call in range(2):
+            x = _x(rc.n, case, call)
+            xd = g.dev(x)
+            if mode in ("call", "in_place", "phased"):
+                if mode == "call":
+                    rc.gpu_call(xd)
+                    y = rc.y
+                elif mode == "in_place":
+                    rc.gpu_call(xd, y=xd)
+                    y = xd
+                else:
+                    B.echo_call_entry(rc.st, xd, rc.send_c, rc.send_s)
+                    B.echo_call_reduce(rc.st, xd, rc.slot(rc.recv_d, 0), rc.slot(rc.recv_d, 1),
+                                       rc.own_c, rc.own_s, rc.y)
+                    B.echo_call_exit(rc.st, rc.slot(rc.gath_d, 0), rc.slot(rc.gath_d, 1), rc.y)
+                    y = rc.y
+                rc.check(rc.oracle_call(x), y=y)
+            elif mode == "plain":
+                B.echo_call_plain(P, rank, xd, rc.slot(rc.recv_d, 0), rc.slot(rc.recv_d, 1),
+                                  rc.slot(rc.gath_d, 0), rc.slot(rc.gath_d, 1), rc.send_c, rc.send_s,
+                                  rc.own_c, rc.own_s, rc.y, bits=bits)
+                want = orc.call(P, rank, x, None, None, rc.slot(rc.recv, 0), rc.slot(rc.recv, 1),
+                                rc.slot(rc.gath, 0), rc.slot(rc.gath, 1), comp=False, bits=bits)
+                rc.check(want)
+            else:
+                y_own = g.empty_bf16(rc.Cn)
+                B.echo_rs_call(rc.st, xd, rc.slot(rc.recv_d, 0), rc.slot(rc.recv_d, 1), rc.send_c,
+                               rc.send_s, y_own)
+                want = orc.rs_call(P, rank, x, rc.mf, rc.ms, rc.slot(rc.recv, 0), rc.slot(rc.recv, 1),
+                                   bits=bits)
+                eq(g.host(y_own, np.uint16), want["y_own"], what + " y_own")
+                eq(g.host(rc.mfd, np.float32), rc.mf, what + " m_fast")
+                eq(g.host(rc.msd, np.float32), rc.ms, what + " m_slow")
+                cb = rc.Cn if bits == 8 else rc.Cn // 2
+                sc = g.host(rc.send_c, np.uint8)
+                for j in range(P):
+                    if j != rank:
+                        eq(sc[j * cb:(j + 1) * cb], want["send_codes"][j * cb:(j + 1) * cb],
+                           what + f" send chunk {j}")
