@@ -429,7 +429,9 @@ def run_workload(args) -> int:
     best = min(eager_ms, graph_ms) if graph_ms else eager_ms
     per_call = step_bytes(n, P)
     out = {
-        "metric": f"GB/s of bf16 payload through fused Echo rank pipeline @{args.workload} workload; % HBM peak", "value": round(2.0 * n * calls / (best * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "metric": f"GB/s of bf16 payload through fused Echo rank pipeline @{args.workload} workload; "
+                  "% HBM peak",
+        "value": round(2.0 * n * calls / (best * 1e-3) / 1e9, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(best, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
