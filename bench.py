@@ -107,6 +107,20 @@ def make_workload(N: int, P: int, rank: int, seed: int = 0):
     return x, recv, gath
 
 
+def host_cpu() -> str:
+    """CPU model and logical CPU count of the host the oracle ran on."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs visible"
+
+
 def cpu_baseline(x, recv, gath, P: int, rank: int, n_sample: int, calls: int):
     """The CPU oracle as it stands (one thread), rank-mode calls on the first
     n_sample elements of the same workload (the sample's chunks are prefixes
@@ -134,6 +148,7 @@ def cpu_baseline(x, recv, gath, P: int, rank: int, n_sample: int, calls: int):
         "kind": "oracle",
         "sample": (f"{calls} rank-mode calls (P={P}, rank {rank}) on the first {n_sample} "
                    f"elements of the workload, averages carried; {dt:.1f} s on 1 thread"),
+        "host": host_cpu(),
     }
 
 
@@ -478,6 +493,7 @@ def workload_cpu_baseline(xs, recv_h, gath_h, P: int, rank: int, nstates: int, b
         "kind": "oracle",
         "sample": f"the first {done} of the step's {calls} rank-mode calls (P={P}, rank {rank}), "
                   f"{n} elements each, state carried; {spent:.2f} s on one host thread",
+        "host": host_cpu(),
     }
 
 
