@@ -3,6 +3,9 @@
 Argument marshalling only: every step of the pipeline runs in the HIP
 kernels of libecho.so.  PyTorch provides device memory and streams: tensors
 are passed by address, the stream defaults to torch's current stream.
+Tensor arguments are checked on the host before the call (on the GPU,
+contiguous, at least the bytes the call reads or writes); plain integer
+addresses are passed through unchecked.
 
 Functions keep the C names (echo_state_init, echo_encode, ...) and raise
 EchoError on a non-zero status.  There is no fallback: if libecho.so is
@@ -89,22 +92,41 @@ def _check(status: int, where: str) -> None:
         raise EchoError(status, where)
 
 
-def _ptr(t):
-    """Device address of a tensor (None -> NULL); plain ints pass through."""
+def _cb(n: int, bits: int) -> int:
+    """bytes of the codes of n elements"""
+    return n if bits == 8 else n // 2
+
+
+def _sb(n: int) -> int:
+    """bytes of the scales of n elements"""
+    return (n // GROUP) * 4
+
+
+def _ptr(t, nbytes: int = 0, what: str = "buffer"):
+    """Device address of a tensor (None -> NULL; plain ints pass through
+    unchecked).  A tensor must live on the GPU, be contiguous and hold at
+    least nbytes: the library cannot see a host pointer or the end of a
+    buffer, and a kernel given either would fault."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"{what}: a GPU tensor is required (got one on {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: the tensor must be contiguous")
+    if t.nbytes < nbytes:
+        raise ValueError(f"{what}: holds {t.nbytes} bytes, the call needs {nbytes}")
     return t.data_ptr()
 
 
 _PTR16 = C.c_void_p * MAX_RANKS
 
 
-def _ptrs(ts):
+def _ptrs(ts, nbytes: int = 0, what: str = "buffers"):
     """void*[>= MAX_RANKS] of device addresses: entries past the list are NULL,
     which the library rejects instead of reading past the array."""
-    vals = [None if t is None else (t if isinstance(t, int) else t.data_ptr()) for t in ts]
+    vals = [_ptr(t, nbytes, f"{what}[{i}]") for i, t in enumerate(ts)]
     if len(vals) <= MAX_RANKS:
         return _PTR16(*vals)
     return (C.c_void_p * len(vals))(*vals)
@@ -124,7 +146,8 @@ class EchoState:
     def __init__(self, m_fast: torch.Tensor, m_slow: torch.Tensor, n: int, nranks: int, rank: int,
                  bits: int = 4):
         self.m_fast, self.m_slow = m_fast, m_slow  # keep the buffers alive
-        self.c = EchoStateC(_ptr(m_fast), _ptr(m_slow), int(n), int(nranks), int(rank), int(bits), 0)
+        self.c = EchoStateC(_ptr(m_fast, 4 * int(n), "m_fast"), _ptr(m_slow, 4 * int(n), "m_slow"),
+                            int(n), int(nranks), int(rank), int(bits), 0)
 
     @property
     def bits(self) -> int:
@@ -146,18 +169,24 @@ class EchoState:
     def rank(self) -> int:
         return self.c.rank
 
+    def sizes(self):
+        """(n, chunk, bits) of this state's calls"""
+        n, P = self.c.n, self.c.nranks
+        return n, (n // P if P > 0 else 0), self.c.bits
+
 
 def echo_state_init(m_fast, m_slow, n, nranks, rank, stream=None, bits: int = 4) -> EchoState:
     st = EchoState(m_fast, m_slow, n, nranks, rank)
-    _check(lib.echo_state_init(C.byref(st.c), _ptr(m_fast), _ptr(m_slow), int(n), int(nranks),
+    _check(lib.echo_state_init(C.byref(st.c), st.c.m_fast, st.c.m_slow, int(n), int(nranks),
                                int(rank), _stream(stream)), "echo_state_init")
     st.bits = bits
     return st
 
 
 def echo_encode(st: EchoState, x, codes, scales, stream=None) -> None:
-    _check(lib.echo_encode(C.byref(st.c), _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)),
-           "echo_encode")
+    n, _, bits = st.sizes()
+    _check(lib.echo_encode(C.byref(st.c), _ptr(x, 2 * n, "x"), _ptr(codes, _cb(n, bits), "codes"),
+                           _ptr(scales, _sb(n), "scales"), _stream(stream)), "echo_encode")
 
 
 def echo_reduce_shard(shard_codes, shard_scales, out_codes, out_scales, out_y=None, out_e2=None,
@@ -165,16 +194,20 @@ def echo_reduce_shard(shard_codes, shard_scales, out_codes, out_scales, out_y=No
     P = len(shard_codes)
     if chunk_n is None:
         chunk_n = out_codes.numel() * (1 if bits == 8 else 2)
-    _check(lib.echo_reduce_shard(P, int(chunk_n), int(bits), _ptrs(shard_codes), _ptrs(shard_scales),
-                                 _ptr(out_codes), _ptr(out_scales), _ptr(out_y), _ptr(out_e2),
-                                 _stream(stream)), "echo_reduce_shard")
+    cn = int(chunk_n)
+    _check(lib.echo_reduce_shard(P, cn, int(bits), _ptrs(shard_codes, _cb(cn, bits), "shard_codes"),
+                                 _ptrs(shard_scales, _sb(cn), "shard_scales"),
+                                 _ptr(out_codes, _cb(cn, bits), "out_codes"),
+                                 _ptr(out_scales, _sb(cn), "out_scales"), _ptr(out_y, 2 * cn, "out_y"),
+                                 _ptr(out_e2, 4 * cn, "out_e2"), _stream(stream)), "echo_reduce_shard")
 
 
 def echo_decode(codes, scales, y, n=None, stream=None, bits: int = 4) -> None:
     if n is None:
         n = y.numel()
-    _check(lib.echo_decode(int(n), int(bits), _ptr(codes), _ptr(scales), _ptr(y), _stream(stream)),
-           "echo_decode")
+    n = int(n)
+    _check(lib.echo_decode(n, int(bits), _ptr(codes, _cb(n, bits), "codes"), _ptr(scales, _sb(n), "scales"),
+                           _ptr(y, 2 * n, "y"), _stream(stream)), "echo_decode")
 
 
 def echo_stream_copy(src, dst, nbytes=None, stream=None) -> None:
@@ -182,37 +215,57 @@ def echo_stream_copy(src, dst, nbytes=None, stream=None) -> None:
     against); nbytes defaults to dst's size in bytes."""
     if nbytes is None:
         nbytes = dst.numel() * dst.element_size()
-    _check(lib.echo_stream_copy(_ptr(src), _ptr(dst), int(nbytes), _stream(stream)), "echo_stream_copy")
+    nb = int(nbytes)
+    _check(lib.echo_stream_copy(_ptr(src, nb, "src"), _ptr(dst, nb, "dst"), nb, _stream(stream)),
+           "echo_stream_copy")
 
 
 def echo_update(st: EchoState, x, codes1, scales1, e2_own, stream=None) -> None:
-    _check(lib.echo_update(C.byref(st.c), _ptr(x), _ptr(codes1), _ptr(scales1), _ptr(e2_own),
+    n, cn, bits = st.sizes()
+    _check(lib.echo_update(C.byref(st.c), _ptr(x, 2 * n, "x"), _ptr(codes1, _cb(n, bits), "codes1"),
+                           _ptr(scales1, _sb(n), "scales1"), _ptr(e2_own, 4 * cn, "e2_own"),
                            _stream(stream)), "echo_update")
 
 
 def echo_call_entry(st: EchoState, x, send_codes, send_scales, stream=None) -> None:
-    _check(lib.echo_call_entry(C.byref(st.c), _ptr(x), _ptr(send_codes), _ptr(send_scales),
-                               _stream(stream)), "echo_call_entry")
+    n, _, bits = st.sizes()
+    _check(lib.echo_call_entry(C.byref(st.c), _ptr(x, 2 * n, "x"), _ptr(send_codes, _cb(n, bits), "send_codes"),
+                               _ptr(send_scales, _sb(n), "send_scales"), _stream(stream)), "echo_call_entry")
 
 
 def echo_call_reduce(st: EchoState, x, recv_codes, recv_scales, own_codes2, own_scales2, y,
                      stream=None) -> None:
-    _check(lib.echo_call_reduce(C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
-                                _ptr(own_codes2), _ptr(own_scales2), _ptr(y), _stream(stream)),
-           "echo_call_reduce")
+    n, cn, bits = st.sizes()
+    _check(lib.echo_call_reduce(C.byref(st.c), _ptr(x, 2 * n, "x"),
+                                _ptrs(recv_codes, _cb(cn, bits), "recv_codes"),
+                                _ptrs(recv_scales, _sb(cn), "recv_scales"),
+                                _ptr(own_codes2, _cb(cn, bits), "own_codes2"),
+                                _ptr(own_scales2, _sb(cn), "own_scales2"), _ptr(y, 2 * n, "y"),
+                                _stream(stream)), "echo_call_reduce")
 
 
 def echo_call_exit(st: EchoState, gath_codes, gath_scales, y, stream=None) -> None:
-    _check(lib.echo_call_exit(C.byref(st.c), _ptrs(gath_codes), _ptrs(gath_scales), _ptr(y),
+    n, cn, bits = st.sizes()
+    _check(lib.echo_call_exit(C.byref(st.c), _ptrs(gath_codes, _cb(cn, bits), "gath_codes"),
+                              _ptrs(gath_scales, _sb(cn), "gath_scales"), _ptr(y, 2 * n, "y"),
                               _stream(stream)), "echo_call_exit")
+
+
+def _call_args(n, cn, bits, x, recv_codes, recv_scales, gath_codes, gath_scales, send_codes,
+               send_scales, own_codes2, own_scales2, y):
+    """checked addresses of one call's buffers (n elements, chunk cn, bits)"""
+    return (_ptr(x, 2 * n, "x"), _ptrs(recv_codes, _cb(cn, bits), "recv_codes"),
+            _ptrs(recv_scales, _sb(cn), "recv_scales"), _ptrs(gath_codes, _cb(cn, bits), "gath_codes"),
+            _ptrs(gath_scales, _sb(cn), "gath_scales"), _ptr(send_codes, _cb(n, bits), "send_codes"),
+            _ptr(send_scales, _sb(n), "send_scales"), _ptr(own_codes2, _cb(cn, bits), "own_codes2"),
+            _ptr(own_scales2, _sb(cn), "own_scales2"), _ptr(y, 2 * n, "y"))
 
 
 def echo_call(st: EchoState, x, recv_codes, recv_scales, gath_codes, gath_scales, send_codes,
               send_scales, own_codes2, own_scales2, y, stream=None) -> None:
-    _check(lib.echo_call(C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
-                         _ptrs(gath_codes), _ptrs(gath_scales), _ptr(send_codes),
-                         _ptr(send_scales), _ptr(own_codes2), _ptr(own_scales2), _ptr(y),
-                         _stream(stream)), "echo_call")
+    _check(lib.echo_call(C.byref(st.c), *_call_args(*st.sizes(), x, recv_codes, recv_scales, gath_codes,
+                                                    gath_scales, send_codes, send_scales, own_codes2,
+                                                    own_scales2, y), _stream(stream)), "echo_call")
 
 
 def echo_call_plain(nranks, rank, x, recv_codes, recv_scales, gath_codes, gath_scales,
@@ -220,31 +273,43 @@ def echo_call_plain(nranks, rank, x, recv_codes, recv_scales, gath_codes, gath_s
                     stream=None, bits: int = 4) -> None:
     if n is None:
         n = x.numel()
-    _check(lib.echo_call_plain(int(nranks), int(rank), int(n), int(bits), _ptr(x), _ptrs(recv_codes),
-                               _ptrs(recv_scales), _ptrs(gath_codes), _ptrs(gath_scales),
-                               _ptr(send_codes), _ptr(send_scales), _ptr(own_codes2),
-                               _ptr(own_scales2), _ptr(y), _stream(stream)), "echo_call_plain")
+    n, P = int(n), int(nranks)
+    cn = n // P if P > 0 else 0
+    _check(lib.echo_call_plain(P, int(rank), n, int(bits),
+                               *_call_args(n, cn, int(bits), x, recv_codes, recv_scales, gath_codes,
+                                           gath_scales, send_codes, send_scales, own_codes2,
+                                           own_scales2, y), _stream(stream)), "echo_call_plain")
 
 
 def echo_reduce_shard_sum(shard_codes, shard_scales, out_y, out_e2=None, chunk_n=None,
                           stream=None, bits: int = 4) -> None:
     if chunk_n is None:
         chunk_n = out_y.numel()
-    _check(lib.echo_reduce_shard_sum(len(shard_codes), int(chunk_n), int(bits), _ptrs(shard_codes),
-                                     _ptrs(shard_scales), _ptr(out_y), _ptr(out_e2),
+    cn = int(chunk_n)
+    _check(lib.echo_reduce_shard_sum(len(shard_codes), cn, int(bits),
+                                     _ptrs(shard_codes, _cb(cn, bits), "shard_codes"),
+                                     _ptrs(shard_scales, _sb(cn), "shard_scales"),
+                                     _ptr(out_y, 2 * cn, "out_y"), _ptr(out_e2, 4 * cn, "out_e2"),
                                      _stream(stream)), "echo_reduce_shard_sum")
 
 
 def echo_rs_reduce(st: EchoState, x, recv_codes, recv_scales, y_own, stream=None) -> None:
-    _check(lib.echo_rs_reduce(C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
-                              _ptr(y_own), _stream(stream)), "echo_rs_reduce")
+    n, cn, bits = st.sizes()
+    _check(lib.echo_rs_reduce(C.byref(st.c), _ptr(x, 2 * n, "x"),
+                              _ptrs(recv_codes, _cb(cn, bits), "recv_codes"),
+                              _ptrs(recv_scales, _sb(cn), "recv_scales"), _ptr(y_own, 2 * cn, "y_own"),
+                              _stream(stream)), "echo_rs_reduce")
 
 
 def echo_rs_call(st: EchoState, x, recv_codes, recv_scales, send_codes, send_scales, y_own,
                  stream=None) -> None:
-    _check(lib.echo_rs_call(C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
-                            _ptr(send_codes), _ptr(send_scales), _ptr(y_own), _stream(stream)),
-           "echo_rs_call")
+    n, cn, bits = st.sizes()
+    _check(lib.echo_rs_call(C.byref(st.c), _ptr(x, 2 * n, "x"),
+                            _ptrs(recv_codes, _cb(cn, bits), "recv_codes"),
+                            _ptrs(recv_scales, _sb(cn), "recv_scales"),
+                            _ptr(send_codes, _cb(n, bits), "send_codes"),
+                            _ptr(send_scales, _sb(n), "send_scales"), _ptr(y_own, 2 * cn, "y_own"),
+                            _stream(stream)), "echo_rs_call")
 
 
 class PreparedCall:
@@ -258,9 +323,9 @@ class PreparedCall:
                  send_codes, send_scales, own_codes2, own_scales2, y):
         self._keep = (st, x, recv_codes, recv_scales, gath_codes, gath_scales, send_codes,
                       send_scales, own_codes2, own_scales2, y)
-        self._args = (C.byref(st.c), _ptr(x), _ptrs(recv_codes), _ptrs(recv_scales),
-                      _ptrs(gath_codes), _ptrs(gath_scales), _ptr(send_codes), _ptr(send_scales),
-                      _ptr(own_codes2), _ptr(own_scales2), _ptr(y))
+        self._args = (C.byref(st.c), *_call_args(*st.sizes(), x, recv_codes, recv_scales, gath_codes,
+                                                 gath_scales, send_codes, send_scales, own_codes2,
+                                                 own_scales2, y))
         self._fn = lib.echo_call
 
     def __call__(self, stream=None) -> None:

@@ -243,3 +243,18 @@ def test_stream_copy_rejections():
 def test_build_entry_check_matches_header():
     import __graft_entry__ as ge
     ge.check_loaded()
+
+
+def test_binding_refuses_host_tensors_before_calling():
+    """A host tensor would reach a kernel as a bad address: the binding stops
+    it on the host (no library call, so no GPU is touched)."""
+    import torch
+    codes = torch.zeros(64, dtype=torch.uint8)
+    scales = torch.zeros(1)
+    y = torch.zeros(128, dtype=torch.int16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.echo_decode(codes, scales, y, stream=0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.EchoState(torch.zeros(1024), torch.zeros(1024), 1024, 2, 0)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        B.echo_stream_copy(codes, codes.clone(), 64, stream=0)

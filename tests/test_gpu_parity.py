@@ -810,3 +810,27 @@ def test_stream_copy_copies_exactly(nbytes):
     torch.cuda.synchronize()
     assert torch.equal(dst[:nbytes], src)
     assert (g.host(dst[nbytes:], np.uint8) == 0xEE).all()
+
+
+def test_binding_checks_tensor_arguments():
+    """Non-contiguous or undersized tensors are refused on the host with the
+    argument named; the same call with proper buffers runs."""
+    g = gu()
+    P, rank, k = 4, 1, 3
+    case = RankCase(P, rank, k, seed=3)
+    xd = g.dev(x_of(case.n, 1))
+    short_y = g.empty_bf16(case.n - 128)
+    with pytest.raises(ValueError, match="y: holds"):
+        B.echo_call(case.st, xd, case.slot(case.recv_d, 0), case.slot(case.recv_d, 1),
+                    case.slot(case.gath_d, 0), case.slot(case.gath_d, 1), case.send_c, case.send_s,
+                    case.own_c, case.own_s, short_y)
+    strided = torch.empty(2 * case.n, dtype=torch.int16, device=g.DEV)[::2]
+    with pytest.raises(ValueError, match="x: the tensor must be contiguous"):
+        B.echo_call_entry(case.st, strided, case.send_c, case.send_s)
+    bad = case.slot(case.recv_d, 0)
+    bad[(rank + 1) % P] = bad[(rank + 1) % P][:-1]
+    with pytest.raises(ValueError, match=r"recv_codes\[\d+\]: holds"):
+        B.echo_call_reduce(case.st, xd, bad, case.slot(case.recv_d, 1), case.own_c, case.own_s, case.y)
+    torch.cuda.synchronize()
+    case.gpu_call(xd)
+    case.check(case.oracle_call(g.host(xd, np.uint16)))
