@@ -74,3 +74,69 @@ def test_captured_call_sequence_replays_bit_exact(bits):
         g.eq(g.host(mf, np.float32), g.host(want_mf, np.float32), f"replay {replay} m_fast")
         g.eq(g.host(ms, np.float32), g.host(want_ms, np.float32), f"replay {replay} m_slow")
         g.eq(g.host(own_c, np.uint8), g.host(want_c, np.uint8), f"replay {replay} codes2")
+
+
+def test_captured_mixed_schedules_with_a_side_stream():
+    """One captured sequence mixing the entry points: a fused call, the
+    uncompensated call, a reduce-scatter call, and the split schedule whose
+    update runs on a second stream forked and joined inside the capture.
+    Every replay equals the eager run bit for bit."""
+    P, rank, n = 8, 5, 8 * 128 * 6
+    C = n // P
+    xs = [g.dev(I.gaussian_outlier_channels(n // 1024, 1024, I.stream_key("mixed", l))) for l in range(4)]
+    recv = [None if q == rank else tuple(g.dev(t) for t in I.int4_message(C, I.stream_key("mr", q)))
+            for q in range(P)]
+    gath = [None if j == rank else tuple(g.dev(t) for t in I.int4_message(C, I.stream_key("mg", j)))
+            for j in range(P)]
+    sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
+    mf, ms = g.empty_f32(n, 0.0), g.empty_f32(n, 0.0)
+    st = B.EchoState(mf, ms, n, P, rank)
+    send_c, send_s = g.empty_u8(n // 2), g.empty_f32(n // 128)
+    own_c, own_s = g.empty_u8(C // 2), g.empty_f32(C // 128)
+    e2 = g.empty_f32(C, 0.0)
+    ys = [g.empty_bf16(n) for _ in range(3)]
+    y_rs = g.empty_bf16(C)
+    side = torch.cuda.Stream()
+    sh_c = [send_c[rank * C // 2:(rank + 1) * C // 2] if q == rank else recv[q][0] for q in range(P)]
+    sh_s = [send_s[rank * C // 128:(rank + 1) * C // 128] if q == rank else recv[q][1] for q in range(P)]
+
+    def sequence():
+        main = torch.cuda.current_stream()
+        B.echo_call(st, xs[0], sl(recv, 0), sl(recv, 1), sl(gath, 0), sl(gath, 1), send_c, send_s,
+                    own_c, own_s, ys[0], main)
+        B.echo_call_plain(P, rank, xs[1], sl(recv, 0), sl(recv, 1), sl(gath, 0), sl(gath, 1), send_c,
+                          send_s, own_c, own_s, ys[1], stream=main)
+        B.echo_rs_call(st, xs[2], sl(recv, 0), sl(recv, 1), send_c, send_s, y_rs, main)
+        # split schedule: critical path on main, the update on the side stream
+        B.echo_encode(st, xs[3], send_c, send_s, main)
+        B.echo_reduce_shard(sh_c, sh_s, own_c, own_s, ys[2][rank * C:(rank + 1) * C], e2, chunk_n=C,
+                            stream=main)
+        B.echo_call_exit(st, sl(gath, 0), sl(gath, 1), ys[2], main)
+        side.wait_stream(main)
+        B.echo_update(st, xs[3], send_c, send_s, e2, side)
+        main.wait_stream(side)
+
+    outs = lambda: [mf, ms, own_c, own_s, send_c, send_s, e2, y_rs, *ys]  # noqa: E731
+    sequence()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs()]
+
+    warm = torch.cuda.Stream()
+    warm.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(warm):
+        sequence()
+    torch.cuda.current_stream().wait_stream(warm)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sequence()
+    for replay in range(3):
+        mf.zero_()
+        ms.zero_()
+        for t in outs()[2:]:
+            t.view(torch.uint8).fill_(0x3C)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs(), want)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {replay} output {i}"
