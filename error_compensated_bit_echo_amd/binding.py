@@ -53,6 +53,7 @@ _SIGNATURES = {
     "echo_decode": [C.c_int64, C.c_int32, _vp, _vp, _vp, _vp],
     "echo_update": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp, _vp],
     "echo_call_entry": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp],
+    "echo_call_entry_range": [C.POINTER(EchoStateC), _vp, C.c_int32, C.c_int32, _vp, _vp, _vp],
     "echo_call_reduce": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp, _vp, _vp],
     "echo_call_exit": [C.POINTER(EchoStateC), _pp, _pp, _vp, _vp],
     "echo_call": [C.POINTER(EchoStateC), _vp, _pp, _pp, _pp, _pp, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -231,6 +232,15 @@ def echo_call_entry(st: EchoState, x, send_codes, send_scales, stream=None) -> N
     n, _, bits = st.sizes()
     _check(lib.echo_call_entry(C.byref(st.c), _ptr(x, 2 * n, "x"), _ptr(send_codes, _cb(n, bits), "send_codes"),
                                _ptr(send_scales, _sb(n), "send_scales"), _stream(stream)), "echo_call_entry")
+
+
+def echo_call_entry_range(st: EchoState, x, chunk_begin, chunk_end, send_codes, send_scales,
+                          stream=None) -> None:
+    n, _, bits = st.sizes()
+    _check(lib.echo_call_entry_range(C.byref(st.c), _ptr(x, 2 * n, "x"), int(chunk_begin), int(chunk_end),
+                                     _ptr(send_codes, _cb(n, bits), "send_codes"),
+                                     _ptr(send_scales, _sb(n), "send_scales"), _stream(stream)),
+           "echo_call_entry_range")
 
 
 def echo_call_reduce(st: EchoState, x, recv_codes, recv_scales, own_codes2, own_scales2, y,

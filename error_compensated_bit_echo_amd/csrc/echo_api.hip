@@ -235,9 +235,14 @@ void add_remote_inputs(Aliases& al, const echo_state* st, const uint8_t* const* 
   }
 }
 
-int run_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes, float* send_scales,
-              hipStream_t s) {
+// Entry pass over chunks [j0, j1) except the own chunk.  The kernel walks
+// "virtual" groups that leave the own chunk out: chunk j starts at virtual
+// group j*cg before the own chunk and (j-1)*cg after it.
+int run_entry_range(const echo_state* st, const uint16_t* x, int32_t j0, int32_t j1,
+                    uint8_t* send_codes, float* send_scales, hipStream_t s) {
   const Geometry g = geometry(st);
+  const int32_t r = st->rank;
+  const uint32_t chunks = (uint32_t)(j1 - j0) - ((j0 <= r && r < j1) ? 1u : 0u);
   Stage1Args a;
   a.x = x;
   a.mf = st->m_fast;
@@ -245,10 +250,16 @@ int run_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes, floa
   a.codes = send_codes;
   a.scales = send_scales;
   a.e2 = nullptr;
-  a.groups_work = g.groups - g.chunk_groups;
+  a.groups_work = chunks * g.chunk_groups;
+  a.v_base = (uint32_t)(j0 <= r ? j0 : j0 - 1) * g.chunk_groups;
   a.own_g0 = g.own_g0;
   a.own_g1 = g.own_g1;
   return launch_stage1<kEntryFused>(a, st->bits, s);
+}
+
+int run_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes, float* send_scales,
+              hipStream_t s) {
+  return run_entry_range(st, x, 0, st->nranks, send_codes, send_scales, s);
 }
 
 int run_reduce_own(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
@@ -417,6 +428,7 @@ int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* 
   a.scales = scales;
   a.e2 = nullptr;
   a.groups_work = (uint32_t)(n / ECHO_GROUP);
+  a.v_base = 0;
   a.own_g0 = a.own_g1 = 0;
   return launch_stage1<kEncode>(a, st->bits, (hipStream_t)stream);
 }
@@ -508,6 +520,7 @@ int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
   a.scales = const_cast<float*>(scales1);
   a.e2 = e2_own;
   a.groups_work = g.groups;
+  a.v_base = 0;
   a.own_g0 = g.own_g0;
   a.own_g1 = g.own_g1;
   return launch_stage1<kUpdate>(a, st->bits, (hipStream_t)stream);
@@ -515,8 +528,15 @@ int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
 
 int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes,
                     float* send_scales, echo_stream_t stream) {
+  return echo_call_entry_range(st, x, 0, st ? st->nranks : 0, send_codes, send_scales, stream);
+}
+
+int echo_call_entry_range(const echo_state* st, const uint16_t* x, int32_t chunk_begin,
+                          int32_t chunk_end, uint8_t* send_codes, float* send_scales,
+                          echo_stream_t stream) {
   int rc = check_state(st);
   if (rc) return finished(rc);
+  if (chunk_begin < 0 || chunk_end > st->nranks || chunk_begin > chunk_end) return ECHO_ERR_RANKS;
   if (!x || !send_codes || !send_scales) return ECHO_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(send_codes, 16) || !aligned(send_scales, 4))
     return ECHO_ERR_ALIGNMENT;
@@ -528,7 +548,8 @@ int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes
   al.out(st->m_slow, n * 4);
   al.in(x, n * 2);
   if (!al.ok()) return ECHO_ERR_ALIAS;
-  return run_entry(st, x, send_codes, send_scales, (hipStream_t)stream);
+  return run_entry_range(st, x, chunk_begin, chunk_end, send_codes, send_scales,
+                         (hipStream_t)stream);
 }
 
 int echo_call_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,

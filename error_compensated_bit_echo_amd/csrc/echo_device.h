@@ -220,6 +220,8 @@ struct Stage1Args {
   float* scales;          // kEncode/kEntryFused: out [n/128]; kUpdate: in
   const float* e2;        // kUpdate: [own chunk], indexed from own_g0*128
   uint32_t groups_work;   // virtual groups to process
+  uint32_t v_base;        // first virtual group (the own chunk is not counted
+                          // when the mode skips it)
   uint32_t own_g0;        // own chunk, in groups
   uint32_t own_g1;
 };
@@ -246,8 +248,8 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
     for (int u = 0; u < U; ++u) {
       uint32_t v = 2u * (s0 + u) + half;
       ok[u] = (s0 + u < nslices) && (v < a.groups_work);
-      uint32_t gg = v;
-      if (skips_own(MODE)) gg = v < a.own_g0 ? v : v + own_len;
+      uint32_t gg = a.v_base + v;
+      if (skips_own(MODE)) gg = gg < a.own_g0 ? gg : gg + own_len;
       g[u] = ok[u] ? gg : 0u;
       const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
       uint2 xw = make_uint2(0u, 0u);

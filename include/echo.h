@@ -189,6 +189,19 @@ int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
 int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes,
                     float* send_scales, echo_stream_t stream);
 
+/* The entry phase restricted to chunks [chunk_begin, chunk_end), the own
+ * chunk still skipped: for each such chunk j exactly what echo_call_entry
+ * does to chunk j (its part of send_codes / send_scales and of the
+ * averages), nothing else.  Ranges that cover [0, P) once, in any order and
+ * on any streams the caller orders before the reduce phase, together equal
+ * one echo_call_entry; a transport can send chunk j to rank j while later
+ * chunks are still being encoded.  Buffers are the full-size ones of
+ * echo_call_entry.  0 <= chunk_begin <= chunk_end <= P, else ECHO_ERR_RANKS;
+ * an empty range (or the own chunk alone) enqueues nothing. */
+int echo_call_entry_range(const echo_state* st, const uint16_t* x, int32_t chunk_begin,
+                          int32_t chunk_end, uint8_t* send_codes, float* send_scales,
+                          echo_stream_t stream);
+
 /* Reduce phase over the own chunk: correction and stage-1 quantization of
  * the own elements (kept in registers, never stored), the rank-order sum with
  * the P-1 incoming shards recv_codes[q] / recv_scales[q] (host arrays of

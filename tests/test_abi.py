@@ -25,7 +25,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for want in ("echo_state_init", "echo_encode", "echo_reduce_shard", "echo_decode",
                  "echo_update", "echo_call", "echo_call_entry", "echo_call_reduce",
-                 "echo_call_exit", "echo_call_plain", "echo_reduce_shard_sum", "echo_rs_reduce",
+                 "echo_call_exit", "echo_call_entry_range", "echo_call_plain", "echo_reduce_shard_sum",
+                 "echo_rs_reduce",
                  "echo_rs_call", "echo_stream_copy", "echo_get_config", "echo_status_string",
                  "echo_version"):
         assert want in names
@@ -229,6 +230,17 @@ def test_empty_calls_are_noops():
     assert rc(B.echo_decode, None, None, None, -128) == -2
     assert rc(B.echo_reduce_shard, nulls * 3, nulls * 3, None, None, None, None, 0) == -4
     assert rc(B.echo_reduce_shard_sum, nulls, nulls, None, None, 0, bits=2) == -7
+
+
+def test_entry_range_rejections():
+    s4 = st(n=4096, P=4, rank=1)
+    assert rc(B.echo_call_entry_range, s4, 3 * A, -1, 2, 50 * A, 51 * A) == -4
+    assert rc(B.echo_call_entry_range, s4, 3 * A, 0, 5, 50 * A, 51 * A) == -4
+    assert rc(B.echo_call_entry_range, s4, 3 * A, 3, 2, 50 * A, 51 * A) == -4
+    assert rc(B.echo_call_entry_range, s4, None, 0, 4, 50 * A, 51 * A) == -1
+    assert rc(B.echo_call_entry_range, s4, 3 * A, 0, 4, 3 * A + 16, 51 * A) == -6  # codes over x
+    s4.bits = 6
+    assert rc(B.echo_call_entry_range, s4, 3 * A, 0, 4, 50 * A, 51 * A) == -7
 
 
 def test_stream_copy_rejections():

@@ -834,3 +834,35 @@ def test_binding_checks_tensor_arguments():
     torch.cuda.synchronize()
     case.gpu_call(xd)
     case.check(case.oracle_call(g.host(xd, np.uint16)))
+
+
+@pytest.mark.parametrize("P,rank,k,bits", [(1, 0, 3, 4), (3, 1, 5, 4), (8, 0, 4, 4), (8, 5, 3, 8),
+                                           (16, 7, 2, 4), (16, 0, 3, 8)])
+def test_entry_in_chunk_ranges_then_per_chunk_exit(P, rank, k, bits):
+    """The pipelined form of a call: the entry pass in chunk ranges (shuffled,
+    half of them on a second stream), the reduce, then the exit one gathered
+    chunk at a time with echo_decode -- against the oracle's call, twice in a
+    row (the averages carried)."""
+    g = gu()
+    rng = np.random.default_rng(1000 * P + 10 * rank + bits)
+    case = RankCase(P, rank, k, seed=4000 + P, bits=bits)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    C = case.Cn
+    for call in range(2):
+        x = x_of(case.n, 77 + call)
+        xd = g.dev(x)
+        cuts = sorted(set(rng.integers(0, P + 1, size=3).tolist()) | {0, P})
+        ranges = list(zip(cuts[:-1], cuts[1:]))
+        rng.shuffle(ranges)
+        side.wait_stream(main)
+        for i, (j0, j1) in enumerate(ranges):
+            B.echo_call_entry_range(case.st, xd, j0, j1, case.send_c, case.send_s, side if i % 2 else main)
+        main.wait_stream(side)
+        B.echo_call_reduce(case.st, xd, case.slot(case.recv_d, 0), case.slot(case.recv_d, 1),
+                           case.own_c, case.own_s, case.y)
+        for j in range(P):
+            if j == rank:
+                continue
+            B.echo_decode(case.gath_d[j][0], case.gath_d[j][1], case.y[j * C:(j + 1) * C], n=C, bits=bits)
+        case.check(case.oracle_call(x))
