@@ -3,9 +3,12 @@
  *   c_abi_check cpu   library facts, argument rejections and empty calls;
  *                     makes no HIP call, so it runs without a GPU
  *   c_abi_check gpu   rank 1 of P = 4 on hipMalloc'd buffers: three fused
- *                     calls with the averages carried, then the same three
- *                     calls through the phased entry points on a second
- *                     state, each checked bit for bit against the CPU oracle
+ *                     calls with the averages carried, the same three calls
+ *                     through the phased entry points on a second state, and
+ *                     through the pipelined form (entry one chunk at a time in
+ *                     reverse order, reduce, exit one gathered chunk at a time
+ *                     with echo_decode) on a third, each checked bit for bit
+ *                     against the CPU oracle
  *
  * Prints "ok" and exits 0 on success.  Test infrastructure: it links the
  * oracle (liborc.so) beside the library only to compare them. */
@@ -161,13 +164,13 @@ static void check_gpu(void) {
   uint16_t* o_y = (uint16_t*)malloc((size_t)n * 2);
   if (!omf || !oms || !o_send_c || !o_send_s || !o_own_c || !o_own_s || !o_y) FAIL("out of host memory");
 
-  /* device state (two: fused and phased) and outputs */
-  float *mf[2], *ms[2];
-  echo_state st[2];
+  /* device state (three: fused, phased, pipelined) and outputs */
+  float *mf[3], *ms[3];
+  echo_state st[3];
   uint16_t *dx, *dy;
   uint8_t *send_c, *own_c;
   float *send_s, *own_s;
-  for (int v = 0; v < 2; ++v) {
+  for (int v = 0; v < 3; ++v) {
     HIP(hipMalloc((void**)&mf[v], (size_t)n * sizeof(float)));
     HIP(hipMalloc((void**)&ms[v], (size_t)n * sizeof(float)));
     EXPECT(echo_state_init(&st[v], mf[v], ms[v], n, P, RANK, NULL) == ECHO_SUCCESS, "state init");
@@ -181,7 +184,7 @@ static void check_gpu(void) {
   hipStream_t s;
   HIP(hipStreamCreate(&s));
 
-  for (int v = 0; v < 2; ++v) {
+  for (int v = 0; v < 3; ++v) {
     memset(omf, 0, (size_t)n * sizeof(float));
     memset(oms, 0, (size_t)n * sizeof(float));
     for (int c = 0; c < 3; ++c) {
@@ -190,19 +193,32 @@ static void check_gpu(void) {
         EXPECT(echo_call(&st[0], dx, dc[0], ds[0], dc[1], ds[1], send_c, send_s, own_c, own_s, dy,
                          (echo_stream_t)s) == ECHO_SUCCESS,
                "echo_call");
-      } else {
+      } else if (v == 1) {
         EXPECT(echo_call_entry(&st[1], dx, send_c, send_s, (echo_stream_t)s) == ECHO_SUCCESS, "entry");
         EXPECT(echo_call_reduce(&st[1], dx, dc[0], ds[0], own_c, own_s, dy, (echo_stream_t)s) ==
                    ECHO_SUCCESS,
                "reduce");
         EXPECT(echo_call_exit(&st[1], dc[1], ds[1], dy, (echo_stream_t)s) == ECHO_SUCCESS, "exit");
+      } else {
+        for (int j = P - 1; j >= 0; --j)
+          EXPECT(echo_call_entry_range(&st[2], dx, j, j + 1, send_c, send_s, (echo_stream_t)s) ==
+                     ECHO_SUCCESS,
+                 "entry range");
+        EXPECT(echo_call_reduce(&st[2], dx, dc[0], ds[0], own_c, own_s, dy, (echo_stream_t)s) ==
+                   ECHO_SUCCESS,
+               "reduce");
+        for (int j = 0; j < P; ++j) {
+          if (j == RANK) continue;
+          EXPECT(echo_decode(C, 4, dc[1][j], ds[1][j], dy + j * C, (echo_stream_t)s) == ECHO_SUCCESS,
+                 "decode");
+        }
       }
       HIP(hipStreamSynchronize(s));
       EXPECT(orc_call(P, RANK, n, x[c], omf, oms, (const uint8_t* const*)hc[0], (const float* const*)hs[0],
                       (const uint8_t* const*)hc[1], (const float* const*)hs[1], o_send_c, o_send_s,
                       o_own_c, o_own_s, o_y, 1, 4) == 0,
              "orc_call");
-      expect_equal(dy, o_y, (size_t)n * 2, v ? "phased y" : "y", c);
+      expect_equal(dy, o_y, (size_t)n * 2, v == 0 ? "y" : v == 1 ? "phased y" : "pipelined y", c);
       expect_equal(own_c, o_own_c, cb, "own codes2", c);
       expect_equal(own_s, o_own_s, cs, "own scales2", c);
       expect_equal(mf[v], omf, (size_t)n * sizeof(float), "m_fast", c);
@@ -216,7 +232,7 @@ static void check_gpu(void) {
   }
 
   HIP(hipStreamDestroy(s));
-  for (int v = 0; v < 2; ++v) {
+  for (int v = 0; v < 3; ++v) {
     HIP(hipFree(mf[v]));
     HIP(hipFree(ms[v]));
   }

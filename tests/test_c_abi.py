@@ -39,6 +39,6 @@ def test_c_consumer_without_gpu(tmp_path):
 @pytest.mark.gpu
 def test_c_consumer_on_the_gpu(tmp_path):
     exe = _build(tmp_path)
-    print("c_abi_check gpu: P=4 rank=1 n=2560, fused and phased", flush=True)
+    print("c_abi_check gpu: P=4 rank=1 n=2560, fused, phased and pipelined", flush=True)
     r = subprocess.run([str(exe), "gpu"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
