@@ -335,6 +335,80 @@ def practical_ceiling(B, torch, stream, nbytes: int = 1 << 30, reps: int = 10) -
             "GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
+def run_sweep(args) -> int:
+    """Time per fused call (rank 0 of P = 8) over message sizes from 2^16 to
+    2^29 elements; small sizes replay a captured graph of 64 calls so the
+    figure is the GPU's, not the host's."""
+    import torch
+
+    from error_compensated_bit_echo_amd import binding as B
+
+    dev = torch.device("cuda:0")
+    P, rank = 8, 0
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    rows = []
+    for log2n in range(16, 30):
+        n = 1 << log2n
+        C = n // P
+        print(f"bench: sweep n=2^{log2n}", file=sys.stderr, flush=True)
+        x = torch.randn(n, device=dev, generator=gen).to(torch.bfloat16).view(torch.int16)
+
+        def msg():
+            c = torch.randint(0, 256, (C // 2,), device=dev, generator=gen, dtype=torch.uint8)
+            c = torch.where((c & 15) == 8, c ^ 1, c)
+            c = torch.where((c >> 4) == 8, c ^ 16, c)
+            return c, torch.rand(C // 128, device=dev, generator=gen) * 0.5 + 0.05
+
+        recv = [None if q == rank else msg() for q in range(P)]
+        gath = [None if j == rank else msg() for j in range(P)]
+        sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
+        mf, ms = torch.empty(n, device=dev), torch.empty(n, device=dev)
+        st = B.echo_state_init(mf, ms, n, P, rank)
+        send_c = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+        send_s = torch.empty(n // 128, device=dev)
+        own_c = torch.empty(C // 2, dtype=torch.uint8, device=dev)
+        own_s = torch.empty(C // 128, device=dev)
+        y = torch.empty(n, dtype=torch.int16, device=dev)
+        call = B.echo_call_prepare(st, x, sl(recv, 0), sl(recv, 1), sl(gath, 0), sl(gath, 1), send_c,
+                                   send_s, own_c, own_s, y)
+        reps = 64 if log2n < 24 else 8
+        if log2n < 24:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(reps):
+                    call(side)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(reps):
+                    call()
+            run = g.replay
+        else:
+            def run():
+                for _ in range(reps):
+                    call()
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (5 * reps)
+        rows.append({"elements": n, "us_per_call": round(us, 2),
+                     "payload_GBps": round(2.0 * n / (us * 1e-6) / 1e9, 1),
+                     "pct_hbm_peak": round(100.0 * step_bytes(n, P) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)})
+        del x, recv, gath, mf, ms, send_c, send_s, own_c, own_s, y, call, st
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "fused Echo call time vs message size (rank 0 of 8)", "unit": "us",
+                      "dtype": "f32", "data": "synthetic", "n_gpus": 1, "sweep": rows}), flush=True)
+    return 0
+
+
 def calibration_copy(dev) -> None:
     """A plain device copy of known size (reads 1 GiB, writes 1 GiB): the
     reference that scales HBM counter readings to bytes."""
@@ -516,6 +590,8 @@ def main() -> int:
                          "the known-size reference for HBM counter runs")
     ap.add_argument("--workload", default="1gb", choices=["1gb", *WORKLOADS],
                     help="1gb (the headline, default) or one of the smaller workloads")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline: time per fused call for 2^16 .. 2^29 elements")
     ap.add_argument("--graph", action="store_true",
                     help="smaller workloads: also time the step captured in a HIP graph")
     args = ap.parse_args()
@@ -524,6 +600,8 @@ def main() -> int:
         print("bench.py measures the per-rank pipeline on one GPU; the library has no "
               "multi-GPU transport, so --gpus must be 1", file=sys.stderr)
         return 2
+    if args.sweep:
+        return run_sweep(args)
     if args.workload != "1gb":
         return run_workload(args)
 
