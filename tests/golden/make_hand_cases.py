@@ -3,9 +3,11 @@
 The expected values here are derived by hand (see each case's "why"); this
 script only lays them out, with every float stored as float.hex() so the
 fixture is exact.  It imports nothing from the library or the oracle.
-Sources: the pages fix "4-bit integer transport" with per-group scaling
-("Tensor-parallel traffic drops to 4 bits", Interpretation; "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication", Abstract); the group size 128, the code
-range [-7, 7], s = amax / 7 and round-half-to-even are the stated readings.
+Sources: the pages fix a transport of 4-bit integer codes ("Tensor-parallel
+traffic drops to 4 bits", Interpretation; "Echo: Error-Compensated 4-Bit
+Tensor-Parallel Communication", Abstract); per-group scaling, the group size
+128, the code range [-7, 7], s = amax / 7 and round-half-to-even are the
+stated readings.
 """
 import json
 import os
