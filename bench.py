@@ -600,6 +600,9 @@ def main() -> int:
         print("bench.py measures the per-rank pipeline on one GPU; the library has no "
               "multi-GPU transport, so --gpus must be 1", file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+        return 2
     if args.sweep:
         return run_sweep(args)
     if args.workload != "1gb":

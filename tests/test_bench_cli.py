@@ -50,3 +50,9 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "--gpus must be 1" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_step_counts_are_checked():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "--steps" in r.stderr
