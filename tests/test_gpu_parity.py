@@ -866,3 +866,39 @@ def test_entry_in_chunk_ranges_then_per_chunk_exit(P, rank, k, bits):
                 continue
             B.echo_decode(case.gath_d[j][0], case.gath_d[j][1], case.y[j * C:(j + 1) * C], n=C, bits=bits)
         case.check(case.oracle_call(x))
+
+
+def test_concurrent_sequences_on_two_streams_from_two_threads():
+    """No global state: two independent call sequences (different P, rank,
+    width and state), each issued from its own host thread on its own stream
+    with no synchronization between them, both equal the oracle."""
+    import threading
+
+    g = gu()
+    cases = [RankCase(8, 3, 6, seed=61, bits=4), RankCase(5, 0, 9, seed=62, bits=8)]
+    inputs = [[x_of(c.n, 6100 + 10 * i + k) for k in range(4)] for i, c in enumerate(cases)]
+    devs = [[g.dev(x) for x in xs] for xs in inputs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    errors = []
+
+    def run(i):
+        try:
+            c, s = cases[i], streams[i]
+            for xd in devs[i]:
+                B.echo_call(c.st, xd, c.slot(c.recv_d, 0), c.slot(c.recv_d, 1), c.slot(c.gath_d, 0),
+                            c.slot(c.gath_d, 1), c.send_c, c.send_s, c.own_c, c.own_s, c.y, s)
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for c, xs in zip(cases, inputs):
+        for x in xs:
+            want = c.oracle_call(x)
+        c.check(want)  # the last call's outputs and the state after all four
