@@ -129,8 +129,13 @@ typedef struct echo_config {
   int64_t max_elements;
 } echo_config;
 
-/* Fill *st (bits = 4) and enqueue zero-fills of m_fast and m_slow (the
- * averages start at zero).  Validates shape, ranks and alignment. */
+/* Set up the compensator of a call sequence ("Tensor-parallel traffic drops
+ * to 4 bits", Interpretation: the correction comes from a fast and a slow
+ * moving average of the errors earlier calls injected; the pages give no
+ * starting value, and this library starts both at zero).  Fills *st (bits = 4)
+ * and enqueues zero-fills of m_fast[n] and m_slow[n] on `stream`; the buffers
+ * stay caller-owned.  Validates shape, ranks, alignment and that the two
+ * buffers do not overlap; nothing is enqueued when a check fails. */
 int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int32_t nranks,
                     int32_t rank, echo_stream_t stream);
 
@@ -160,8 +165,12 @@ int echo_reduce_shard(int32_t nranks, int64_t chunk_n, int32_t bits,
                       uint8_t* out_codes, float* out_scales, uint16_t* out_y, float* out_e2,
                       echo_stream_t stream);
 
-/* Exit pass over n elements: y = bf16(code*scale), round to nearest even.
- * n > 0 and n % 128 == 0. */
+/* Exit pass over n elements ("Echo: Error-Compensated 4-Bit Tensor-Parallel
+ * Communication", Abstract: the all-reduce moves 4-bit codes; the receiver
+ * turns them back into the 16-bit tensor): y[n] = bf16(code*scale), rounded
+ * to nearest even, from codes[n/2] (n bytes at 8 bits) and scales[n/128].
+ * Reads the codes and scales, writes only y; y may not overlap them
+ * (ECHO_ERR_ALIAS).  n % 128 == 0; n == 0 is a no-op. */
 int echo_decode(int64_t n, int32_t bits, const uint8_t* codes, const float* scales, uint16_t* y,
                 echo_stream_t stream);
 
@@ -176,13 +185,22 @@ int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
                 const float* scales1, const float* e2_own, echo_stream_t stream);
 
 /* ---- the fused call, and its three phases --------------------------------- */
-/* The phases split the fused call where a multi-GPU transport would sit:
+/* One all-reduce call of rank `st->rank` with the correction fused into the
+ * entry pass and the averages refreshed from the call's own residual
+ * ("Tensor-parallel traffic drops to 4 bits", Interpretation), over the two-
+ * quantization structure of "Echo: Error-Compensated 4-Bit Tensor-Parallel
+ * Communication", Abstract (each value is quantized once on entry and once
+ * after the wide sum, whatever P is).
+ * The phases split the fused call where a multi-GPU transport would sit:
  * entry -> (all-to-all of stage-1 chunks) -> reduce -> (all-gather of
  * stage-2 chunks) -> exit.  echo_call runs all three on one stream and is
  * bit-identical to echo_encode + echo_reduce_shard + echo_decode +
  * echo_update. */
 
-/* Entry phase over every chunk except the own one: correction, stage-1
+/* Entry phase over every chunk except the own one ("Tensor-parallel traffic
+ * drops to 4 bits", Interpretation: the correction is applied inside the
+ * entry pass; "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication",
+ * Abstract: the first of a value's two quantizations): correction, stage-1
  * quantization into send_codes[n/2] / send_scales[n/128] (the own chunk's
  * bytes are left untouched), and the averages' update with r = d1 - x' on
  * those elements. */
@@ -190,7 +208,9 @@ int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes
                     float* send_scales, echo_stream_t stream);
 
 /* The entry phase restricted to chunks [chunk_begin, chunk_end), the own
- * chunk still skipped: for each such chunk j exactly what echo_call_entry
+ * chunk still skipped ("Tensor-parallel traffic drops to 4 bits",
+ * Interpretation, as echo_call_entry; the split by chunk is this library's,
+ * so that sending can overlap encoding): for each such chunk j exactly what echo_call_entry
  * does to chunk j (its part of send_codes / send_scales and of the
  * averages), nothing else.  Ranges that cover [0, P) once, in any order and
  * on any streams the caller orders before the reduce phase, together equal
@@ -202,7 +222,11 @@ int echo_call_entry_range(const echo_state* st, const uint16_t* x, int32_t chunk
                           int32_t chunk_end, uint8_t* send_codes, float* send_scales,
                           echo_stream_t stream);
 
-/* Reduce phase over the own chunk: correction and stage-1 quantization of
+/* Reduce phase over the own chunk ("Echo: Error-Compensated 4-Bit Tensor-
+ * Parallel Communication", Abstract: the codes are summed in a wide format
+ * and requantized, a value's second and last quantization; "Tensor-parallel
+ * traffic drops to 4 bits", Interpretation: forming the sum exposes the error
+ * the call injected, which refreshes the averages): correction and stage-1 quantization of
  * the own elements (kept in registers, never stored), the rank-order sum with
  * the P-1 incoming shards recv_codes[q] / recv_scales[q] (host arrays of
  * nranks device pointers; slot `rank` is ignored and may be NULL; each shard
@@ -213,14 +237,18 @@ int echo_call_reduce(const echo_state* st, const uint16_t* x, const uint8_t* con
                      const float* const* recv_scales, uint8_t* own_codes2, float* own_scales2,
                      uint16_t* y, echo_stream_t stream);
 
-/* Exit phase over every chunk except the own one: y on chunk j from the
+/* Exit phase over every chunk except the own one ("Echo: Error-Compensated
+ * 4-Bit Tensor-Parallel Communication", Abstract: the gathered 4-bit result
+ * is decoded to the 16-bit output): y on chunk j from the
  * gathered stage-2 chunk gath_codes[j] / gath_scales[j] (host arrays of
  * nranks device pointers; slot `rank` ignored; each codes[n/P/2],
  * scales[n/P/128]). */
 int echo_call_exit(const echo_state* st, const uint8_t* const* gath_codes,
                    const float* const* gath_scales, uint16_t* y, echo_stream_t stream);
 
-/* All three phases, in order, on one stream. */
+/* All three phases, in order, on one stream (the fused call of
+ * "Tensor-parallel traffic drops to 4 bits", Interpretation, with the
+ * averages' update inside the entry and reduce kernels). */
 int echo_call(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
               const float* const* recv_scales, const uint8_t* const* gath_codes,
               const float* const* gath_scales, uint8_t* send_codes, float* send_scales,
@@ -262,14 +290,17 @@ int echo_reduce_shard_sum(int32_t nranks, int64_t chunk_n, int32_t bits,
                           const uint8_t* const* shard_codes, const float* const* shard_scales,
                           uint16_t* out_y, float* out_e2, echo_stream_t stream);
 
-/* Reduce phase of the reduce-scatter: the own chunk's correction and stage-1
+/* Reduce phase of the reduce-scatter ("Tensor-parallel traffic drops to 4
+ * bits", Perspective, for the variant; Interpretation, for the correction and
+ * the refresh of the averages): the own chunk's correction and stage-1
  * quantization in registers, the rank-order sum with the P-1 incoming shards
  * (as echo_call_reduce), y_own[n/P] = bf16(S), and the averages' update on
  * the own chunk with r = e1 + (f32(y_own) - S).  y_own may not overlap x. */
 int echo_rs_reduce(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,
                    const float* const* recv_scales, uint16_t* y_own, echo_stream_t stream);
 
-/* The fused reduce-scatter: echo_call_entry then echo_rs_reduce on one stream.
+/* The fused reduce-scatter ("Tensor-parallel traffic drops to 4 bits",
+ * Perspective): echo_call_entry then echo_rs_reduce on one stream.
  * Bit-identical to echo_encode + echo_reduce_shard_sum (own slot = own
  * stage-1 chunk, out_e2 kept) + echo_update. */
 int echo_rs_call(const echo_state* st, const uint16_t* x, const uint8_t* const* recv_codes,

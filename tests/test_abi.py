@@ -270,3 +270,38 @@ def test_binding_refuses_host_tensors_before_calling():
         B.EchoState(torch.zeros(1024), torch.zeros(1024), 1024, 2, 0)
     with pytest.raises(ValueError, match="GPU tensor"):
         B.echo_stream_copy(codes, codes.clone(), 64, stream=0)
+
+
+# Page titles and the sections of them that the header may cite.
+PAGES = {
+    "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication": ("Abstract",),
+    "Tensor-parallel traffic drops to 4 bits": ("Synopsis", "Interpretation", "Perspective"),
+    "How Echo lets big AI models train faster": ("How Echo keeps errors from snowballing",
+                                                 "What the benchmarks show", "Key facts"),
+}
+# calls that are not steps of the method (measurement and bookkeeping)
+NOT_METHOD = {"echo_stream_copy", "echo_get_config", "echo_status_string", "echo_version"}
+
+
+def declaration_comments():
+    """{function: the comment text between the previous declaration and it}"""
+    src = open(HEADER).read()
+    src = src[src.index("typedef struct echo_config"):]
+    out, last = {}, 0
+    for m in re.finditer(r"^\s*(?:const\s+)?\w+\**\s+\**(echo_\w+)\s*\([^;]*\);", src, re.M):
+        between = src[last:m.start()]
+        out[m.group(1)] = " ".join(re.findall(r"/\*(.*?)\*/", between, flags=re.S))
+        last = m.end()
+    return out
+
+
+def test_every_method_call_cites_a_page_section():
+    comments = declaration_comments()
+    assert set(comments) == set(declared_functions())
+    for name, text in comments.items():
+        if name in NOT_METHOD:
+            continue
+        flat = " ".join(text.replace("*", " ").split())
+        cited = [(t, sec) for t, secs in PAGES.items() for sec in secs
+                 if t.replace("-", "") in flat.replace("- ", "").replace("-", "") and sec in flat]
+        assert cited, f"{name}: its comment cites no page section"
