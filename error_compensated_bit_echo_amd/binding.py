@@ -327,18 +327,29 @@ class PreparedCall:
     pipeline again and again on the same buffers (a serving loop's per-layer
     buffers).  Calling it enqueues the call on `stream` (default: torch's
     current stream).  The tensors are kept alive by this object; their
-    contents may change between calls, their storage may not."""
+    contents may change between calls, their storage may not.
+
+    The buffer sizes were checked for the state as it was when the call was
+    prepared (its n, P, rank and code width).  The library is handed a copy
+    of that state, and a call made after the EchoState changed (say, its
+    `bits` set from 4 to 8) raises instead of launching: the buffers may be
+    too small for the new width."""
 
     def __init__(self, st: EchoState, x, recv_codes, recv_scales, gath_codes, gath_scales,
                  send_codes, send_scales, own_codes2, own_scales2, y):
         self._keep = (st, x, recv_codes, recv_scales, gath_codes, gath_scales, send_codes,
                       send_scales, own_codes2, own_scales2, y)
-        self._args = (C.byref(st.c), *_call_args(*st.sizes(), x, recv_codes, recv_scales, gath_codes,
-                                                 gath_scales, send_codes, send_scales, own_codes2,
-                                                 own_scales2, y))
+        self._st = st
+        self._snap = EchoStateC.from_buffer_copy(st.c)
+        self._args = (C.byref(self._snap), *_call_args(*st.sizes(), x, recv_codes, recv_scales,
+                                                       gath_codes, gath_scales, send_codes, send_scales,
+                                                       own_codes2, own_scales2, y))
         self._fn = lib.echo_call
 
     def __call__(self, stream=None) -> None:
+        if bytes(self._st.c) != bytes(self._snap):
+            raise ValueError("echo_call: the state changed since the call was prepared "
+                             f"(bits {self._snap.bits} -> {self._st.c.bits}); prepare it again")
         rc = self._fn(*self._args, _stream(stream))
         if rc != 0:
             raise EchoError(rc, "echo_call")

@@ -21,11 +21,8 @@ namespace {
 // the whole range, so no wave loops: on MI355X a full grid of short-lived
 // workgroups streams HBM faster than a persistent grid-stride loop (measured
 // on the 1 GB message: 6.15 vs 4.37 TB/s for the entry pass).  The kernels
-// keep their grid-stride loop, so a capped grid stays correct; the cap
-// (2^26 workgroups) keeps gridDim.x * 4 waves inside 32 bits.
-#ifndef ECHO_MAX_BLOCKS
-#define ECHO_MAX_BLOCKS (1u << 26)
-#endif
+// keep their grid-stride loop, so a grid capped at HIP's launch limit
+// (launch_shape.h) stays correct.
 #ifndef ECHO_U_STAGE1
 #define ECHO_U_STAGE1 1
 #endif
@@ -41,17 +38,20 @@ namespace {
 #ifndef ECHO_U_REDUCE_PLAIN
 #define ECHO_U_REDUCE_PLAIN 1
 #endif
-constexpr uint32_t kMaxBlocks = ECHO_MAX_BLOCKS;
 constexpr int kU1 = ECHO_U_STAGE1;  // stage-1 slices (2 groups each) per wave step
 constexpr int kUR = ECHO_U_REDUCE;  // reduce slices per wave step
 constexpr int kUD = ECHO_U_EXIT;    // exit: quads of groups per wave step
 
-uint32_t blocks_for(uint64_t wave_steps) {
-  const uint64_t waves_per_block = kBlock / 64;
-  uint64_t b = (wave_steps + waves_per_block - 1) / waves_per_block;
-  if (b < 1) b = 1;
-  if (b > kMaxBlocks) b = kMaxBlocks;
-  return (uint32_t)b;
+// Launch `kernel` with its one by-value argument struct.  The status is the
+// launch's own (hipLaunchKernel's return value), so an error an earlier,
+// unrelated HIP call left in the thread's last-error slot is neither
+// reported as this call's nor cleared.
+template <typename A>
+int launch(void (*kernel)(A), dim3 grid, hipStream_t s, A arg) {
+  void* argv[] = {&arg};
+  const hipError_t e =
+      hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, dim3(kBlock), argv, 0, s);
+  return e == hipSuccess ? ECHO_SUCCESS : ECHO_ERR_HIP;
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -129,10 +129,8 @@ class Aliases {
   const void* allow_b_ = nullptr;
 };
 
-int launch_status() { return hipGetLastError() == hipSuccess ? ECHO_SUCCESS : ECHO_ERR_HIP; }
-
 #ifndef ECHO_UPDATE_MAX_BLOCKS
-#define ECHO_UPDATE_MAX_BLOCKS ECHO_MAX_BLOCKS
+#define ECHO_UPDATE_MAX_BLOCKS kMaxBlocks
 #endif
 
 // slices per wave step for each stage-1 mode: the uncompensated entry pass
@@ -144,13 +142,10 @@ int launch_stage1(const Stage1Args& a, int bits, hipStream_t s) {
   constexpr int U = u_stage1(MODE);
   const uint64_t nslices = ((uint64_t)a.groups_work + 1) / 2;
   if (nslices == 0) return ECHO_SUCCESS;
-  uint32_t blocks = blocks_for((nslices + U - 1) / U);
-  if (MODE == kUpdate && blocks > (uint32_t)ECHO_UPDATE_MAX_BLOCKS) blocks = ECHO_UPDATE_MAX_BLOCKS;
-  if (bits == 8)
-    hipLaunchKernelGGL((k_stage1<MODE, 8, U>), dim3(blocks), dim3(kBlock), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_stage1<MODE, 4, U>), dim3(blocks), dim3(kBlock), 0, s, a);
-  return launch_status();
+  const uint32_t blocks =
+      blocks_for((nslices + U - 1) / U, MODE == kUpdate ? (uint32_t)ECHO_UPDATE_MAX_BLOCKS : kMaxBlocks);
+  if (bits == 8) return launch(k_stage1<MODE, 8, U>, dim3(blocks), s, a);
+  return launch(k_stage1<MODE, 4, U>, dim3(blocks), s, a);
 }
 
 constexpr int u_reduce(int mode) {
@@ -158,11 +153,9 @@ constexpr int u_reduce(int mode) {
 }
 
 template <int MODE, int P>
-void launch_reduce_p(const ReduceArgs& a, int bits, uint32_t blocks, hipStream_t s) {
-  if (bits == 8)
-    hipLaunchKernelGGL((k_reduce<MODE, 8, P, u_reduce(MODE)>), dim3(blocks), dim3(kBlock), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_reduce<MODE, 4, P, u_reduce(MODE)>), dim3(blocks), dim3(kBlock), 0, s, a);
+int launch_reduce_p(const ReduceArgs& a, int bits, uint32_t blocks, hipStream_t s) {
+  if (bits == 8) return launch(k_reduce<MODE, 8, P, u_reduce(MODE)>, dim3(blocks), s, a);
+  return launch(k_reduce<MODE, 4, P, u_reduce(MODE)>, dim3(blocks), s, a);
 }
 
 template <int MODE>
@@ -173,7 +166,7 @@ int launch_reduce(int P, const ReduceArgs& a, int bits, hipStream_t s) {
   const uint32_t blocks = blocks_for((nslices + U - 1) / U);
   switch (P) {
 #define ECHO_REDUCE_CASE(p) \
-  case p: launch_reduce_p<MODE, p>(a, bits, blocks, s); break;
+  case p: return launch_reduce_p<MODE, p>(a, bits, blocks, s);
     ECHO_REDUCE_CASE(1) ECHO_REDUCE_CASE(2) ECHO_REDUCE_CASE(3) ECHO_REDUCE_CASE(4)
     ECHO_REDUCE_CASE(5) ECHO_REDUCE_CASE(6) ECHO_REDUCE_CASE(7) ECHO_REDUCE_CASE(8)
     ECHO_REDUCE_CASE(9) ECHO_REDUCE_CASE(10) ECHO_REDUCE_CASE(11) ECHO_REDUCE_CASE(12)
@@ -181,20 +174,14 @@ int launch_reduce(int P, const ReduceArgs& a, int bits, hipStream_t s) {
 #undef ECHO_REDUCE_CASE
     default: return ECHO_ERR_RANKS;
   }
-  return launch_status();
 }
 
 int launch_decode(const DecodeArgs& a, uint32_t nseg, int bits, hipStream_t s) {
   const uint64_t nquads = ((uint64_t)a.groups + 3) / 4;
   if (nquads == 0 || nseg == 0) return ECHO_SUCCESS;
-  uint32_t blocks = blocks_for((nquads + kUD - 1) / kUD);
-  const uint32_t cap = kMaxBlocks / nseg > 0 ? kMaxBlocks / nseg : 1;
-  if (blocks > cap) blocks = cap;
-  if (bits == 8)
-    hipLaunchKernelGGL((k_decode<8, kUD>), dim3(blocks, nseg), dim3(kBlock), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_decode<4, kUD>), dim3(blocks, nseg), dim3(kBlock), 0, s, a);
-  return launch_status();
+  const uint32_t blocks = blocks_for((nquads + kUD - 1) / kUD, kMaxBlocks / nseg);
+  if (bits == 8) return launch(k_decode<8, kUD>, dim3(blocks, nseg), s, a);
+  return launch(k_decode<4, kUD>, dim3(blocks, nseg), s, a);
 }
 
 // ---- per-phase argument checks and launches (shared by the fused call) ----
@@ -398,12 +385,11 @@ int echo_state_init(echo_state* st, float* m_fast, float* m_slow, int64_t n, int
   st->bits = 4;
   st->reserved = 0;
   if (shape == kEmpty) return ECHO_SUCCESS;
-  const int64_t n4 = n / 4;
-  int64_t blocks = (n4 + kBlock - 1) / kBlock;
-  if (blocks > (int64_t)kMaxBlocks) blocks = kMaxBlocks;
-  hipLaunchKernelGGL(k_zero2, dim3((uint32_t)blocks), dim3(kBlock), 0, (hipStream_t)stream,
-                     reinterpret_cast<float4*>(m_fast), reinterpret_cast<float4*>(m_slow), n4);
-  return launch_status();
+  Zero2Args z;
+  z.a = reinterpret_cast<float4*>(m_fast);
+  z.b = reinterpret_cast<float4*>(m_slow);
+  z.n4 = n / 4;
+  return launch(k_zero2, dim3(blocks_for_items((uint64_t)z.n4)), (hipStream_t)stream, z);
 }
 
 int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* scales,
@@ -791,12 +777,11 @@ int echo_stream_copy(const void* src, void* dst, int64_t bytes, echo_stream_t st
   al.out(dst, bytes);
   al.in(src, bytes);
   if (!al.ok()) return ECHO_ERR_ALIAS;
-  const int64_t n16 = bytes / 16;
-  int64_t blocks = (n16 + kBlock - 1) / kBlock;
-  if (blocks > (int64_t)kMaxBlocks) blocks = kMaxBlocks;
-  hipLaunchKernelGGL(k_copy16, dim3((uint32_t)blocks), dim3(kBlock), 0, (hipStream_t)stream,
-                     reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), n16);
-  return launch_status();
+  CopyArgs c;
+  c.src = reinterpret_cast<const u32x4*>(src);
+  c.dst = reinterpret_cast<u32x4*>(dst);
+  c.n16 = bytes / 16;
+  return launch(k_copy16, dim3(blocks_for_items((uint64_t)c.n16)), (hipStream_t)stream, c);
 }
 
 }  // extern "C"

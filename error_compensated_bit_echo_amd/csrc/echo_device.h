@@ -25,6 +25,7 @@
 #include <stdint.h>
 
 #include "echo.h"
+#include "launch_shape.h"
 
 namespace echo {
 
@@ -34,10 +35,6 @@ constexpr int kGroup = ECHO_GROUP;
 template <int BITS>
 __host__ __device__ constexpr float qmax_of() { return BITS == 8 ? (float)ECHO_QMAX8 : (float)ECHO_QMAX; }
 constexpr int kMaxRanks = ECHO_MAX_RANKS;
-#ifndef ECHO_BLOCK
-#define ECHO_BLOCK 256
-#endif
-constexpr int kBlock = ECHO_BLOCK;  // threads per workgroup (4 wavefronts)
 
 // Cache policy of the streaming accesses: every byte of the averages, the
 // input and the messages is touched once per call, so loads and stores of
@@ -573,19 +570,31 @@ __global__ __launch_bounds__(kBlock) void k_decode(DecodeArgs a) {
 // zero fill (the averages start at zero); a kernel rather than a memset so
 // the call can sit inside a captured graph
 
-__global__ __launch_bounds__(kBlock) void k_zero2(float4* a, float4* b, int64_t n4) {
+struct Zero2Args {
+  float4* a;
+  float4* b;
+  int64_t n4;  // float4s in each
+};
+
+__global__ __launch_bounds__(kBlock) void k_zero2(Zero2Args z) {
   const int64_t stride = (int64_t)gridDim.x * kBlock;
-  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n4; i += stride) {
-    a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    b[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < z.n4; i += stride) {
+    z.a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    z.b[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
 // a plain streaming copy, 16 bytes per lane (the practical bandwidth ceiling)
-__global__ __launch_bounds__(kBlock) void k_copy16(const u32x4* src, u32x4* dst, int64_t n16) {
+struct CopyArgs {
+  const u32x4* src;
+  u32x4* dst;
+  int64_t n16;  // 16-byte vectors
+};
+
+__global__ __launch_bounds__(kBlock) void k_copy16(CopyArgs c) {
   const int64_t stride = (int64_t)gridDim.x * kBlock;
-  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += stride)
-    st_stream(dst + i, ld_stream(src + i));
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < c.n16; i += stride)
+    st_stream(c.dst + i, ld_stream(c.src + i));
 }
 
 }  // namespace echo

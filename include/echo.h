@@ -101,9 +101,10 @@ extern "C" {
 #define ECHO_ERR_SHAPE -2            /* n or chunk_n out of range / not a multiple */
 #define ECHO_ERR_ALIGNMENT -3        /* a pointer misses its alignment */
 #define ECHO_ERR_RANKS -4            /* P or rank out of range */
-#define ECHO_ERR_HIP -5              /* the HIP runtime reported an error after a launch
-                                        (hipGetLastError: the thread's last error, which
-                                        may predate the call if left unchecked) */
+#define ECHO_ERR_HIP -5              /* the HIP runtime rejected one of the call's kernel
+                                        launches (that launch's own status; an error an
+                                        earlier HIP call left behind is neither reported
+                                        nor cleared) */
 #define ECHO_ERR_ALIAS -6            /* outputs overlap each other or an input */
 #define ECHO_ERR_FORMAT -7           /* code width other than 4 or 8 bits */
 

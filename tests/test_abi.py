@@ -305,3 +305,24 @@ def test_every_method_call_cites_a_page_section():
         cited = [(t, sec) for t, secs in PAGES.items() for sec in secs
                  if t.replace("-", "") in flat.replace("- ", "").replace("-", "") and sec in flat]
         assert cited, f"{name}: its comment cites no page section"
+
+
+def test_prepared_call_refuses_a_changed_state():
+    """A prepared call checked its buffers for the state's width at prepare
+    time; after st.bits changes it raises before reaching the library (the
+    fake addresses below are never handed to a kernel)."""
+    P, n = 4, 4096
+    s4 = st(n=n, P=P, rank=1)
+    cn = n // P
+    recv_c = [None if k == 1 else 10 * A + k * A for k in range(P)]
+    recv_s = [None if k == 1 else 20 * A + k * A for k in range(P)]
+    gath_c = [None if k == 1 else 30 * A + k * A for k in range(P)]
+    gath_s = [None if k == 1 else 40 * A + k * A for k in range(P)]
+    call = B.echo_call_prepare(s4, 3 * A, recv_c, recv_s, gath_c, gath_s, 50 * A, 51 * A, 52 * A,
+                               53 * A, 54 * A)
+    assert call._snap.bits == 4 and cn == 1024
+    s4.bits = 8
+    with pytest.raises(ValueError, match="changed since the call was prepared"):
+        call(stream=0)
+    # the copy the library would read keeps the prepared width
+    assert call._snap.bits == 4

@@ -111,6 +111,42 @@ def test_decode(k, bits):
     eq(g.host(y, np.uint16), orc.decode(c, s, n, bits=bits), "y")
 
 
+def _loaded_hip_runtime():
+    """The HIP runtime this process already loaded (torch's, which libecho
+    shares), opened by its path so both handles are the same library."""
+    import ctypes
+    import re
+
+    with open("/proc/self/maps") as f:
+        paths = sorted(set(re.findall(r"(/\S*libamdhip64\.so\S*)", f.read())))
+    assert paths, "no HIP runtime mapped"
+    hip = ctypes.CDLL(paths[0])
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    hip.hipSetDevice.restype = ctypes.c_int
+    return hip
+
+
+def test_stale_hip_error_is_not_reported_as_the_calls():
+    """An error an earlier, unrelated HIP call left behind (here: selecting a
+    device that does not exist, which the runtime rejects on the host) does
+    not make a valid call return ECHO_ERR_HIP: each call reports its own
+    launches' status."""
+    g = gu()
+    n = 128 * 37
+    c, s = I.int4_message(n, I.stream_key("stale", 0), bits=4)
+    cd, sd = g.dev(c), g.dev(s)
+    y = g.empty_bf16(n)
+    torch.cuda.synchronize()
+    hip = _loaded_hip_runtime()
+    assert hip.hipSetDevice(9999) != 0
+    try:
+        B.echo_decode(cd, sd, y, bits=4)  # raises EchoError on a non-zero status
+    finally:
+        hip.hipGetLastError()  # clear the planted error before torch launches anything
+    torch.cuda.synchronize()
+    eq(g.host(y, np.uint16), orc.decode(c, s, n, bits=4), "y after a stale error")
+
+
 @pytest.mark.parametrize("P,k", SHAPES)
 @pytest.mark.parametrize("bits", [4, 8])
 def test_update(P, k, bits):
