@@ -13,7 +13,8 @@ CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-s
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", *CFLAGS, os.path.join(HERE, "echo_oracle.c"), "-o", LIB + ".tmp", "-lm"]
+    cmd = ["gcc", *CFLAGS, "-pthread", os.path.join(HERE, "echo_oracle.c"),
+           os.path.join(HERE, "echo_oracle_mt.c"), "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

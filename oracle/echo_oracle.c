@@ -34,7 +34,9 @@
 #include <stdlib.h>
 #include <string.h>
 
-static long long g_stage_values[3];
+/* Per thread, so the threaded driver's workers never race on it; the
+ * counting pins call the single-thread functions from one thread. */
+static _Thread_local long long g_stage_values[3];
 
 void orc_counters_reset(void) { memset(g_stage_values, 0, sizeof(g_stage_values)); }
 
@@ -224,7 +226,13 @@ void orc_update(int64_t n, int nranks, int rank, const uint16_t* x, float* m_fas
                 const float* e2_own, float* r_out, int bits) {
   int64_t chunk = n / nranks;
   int64_t own0 = (int64_t)rank * chunk, own1 = own0 + chunk;
-  for (int64_t i = 0; i < n; ++i) {
+  orc_update_span(0, n, own0, own1, x, m_fast, m_slow, codes1, scales1, e2_own, r_out, bits);
+}
+
+void orc_update_span(int64_t i0, int64_t i1, int64_t own0, int64_t own1, const uint16_t* x,
+                     float* m_fast, float* m_slow, const uint8_t* codes1, const float* scales1,
+                     const float* e2_own, float* r_out, int bits) {
+  for (int64_t i = i0; i < i1; ++i) {
     float xp = corrected_input(x[i], m_fast[i], m_slow[i], 1);
     float e1 = dequant(codes1, scales1, i, bits) - xp;
     float r = e1;

@@ -91,6 +91,13 @@ void orc_update(int64_t n, int nranks, int rank, const uint16_t* x, float* m_fas
                 float* m_slow, const uint8_t* codes1, const float* scales1,
                 const float* e2_own, float* r_out, int bits);
 
+/* orc_update over the element range [i0, i1) only, with the own chunk given
+ * as [own0, own1) (absolute indices into every array; e2_own is indexed
+ * from own0).  orc_update is this over [0, n). */
+void orc_update_span(int64_t i0, int64_t i1, int64_t own0, int64_t own1, const uint16_t* x,
+                     float* m_fast, float* m_slow, const uint8_t* codes1, const float* scales1,
+                     const float* e2_own, float* r_out, int bits);
+
 /* One call in rank mode (rank p of P): incoming shards recv_*[q] (q != p,
  * each covering chunk p) and gathered outputs gath_*[j] (j != p, each
  * covering chunk j) are inputs.  Writes send_* for every chunk except p,
@@ -135,6 +142,18 @@ int orc_rs_call(int nranks, int rank, int64_t n, const uint16_t* x, float* m_fas
 int orc_rs_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const* m_fast,
                     float* const* m_slow, uint16_t* y, float* const* xp, float* const* r,
                     int comp, int bits);
+
+/* ---- threaded driver (echo_oracle_mt.c) --------------------------------------
+ * orc_call with its steps split over `threads` host threads by disjoint
+ * ranges of whole groups.  Each thread runs the step functions above on its
+ * range, so every output is bit-identical to orc_call's for any thread count
+ * (a thread count below 1 is taken as 1).  The quantizer counters are not
+ * kept.  Returns 0, or -1 on bad arguments / allocation failure. */
+int orc_call_mt(int threads, int nranks, int rank, int64_t n, const uint16_t* x, float* m_fast,
+                float* m_slow, const uint8_t* const* recv_codes, const float* const* recv_scales,
+                const uint8_t* const* gath_codes, const float* const* gath_scales,
+                uint8_t* send_codes, float* send_scales, uint8_t* own_codes2,
+                float* own_scales2, uint16_t* y, int comp, int bits);
 
 #ifdef __cplusplus
 }

@@ -60,6 +60,10 @@ def _load():
                               C.c_int]),
         "orc_call": (C.c_int, [C.c_int, C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _vp, _vp, _vp, C.c_int, C.c_int]),
+        "orc_call_mt": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, C.c_int]),
+        "orc_update_span": (None, [C.c_int64, C.c_int64, C.c_int64, C.c_int64, _vp, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, C.c_int]),
         "orc_simulate": (C.c_int, [C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _vp, C.c_int, C.c_int]),
         "orc_reduce_chunk_sum": (None, [C.c_int, C.c_int64, _vp, _vp, _vp, _vp, C.c_int]),
@@ -215,25 +219,33 @@ def update(x, m_fast, m_slow, codes1, scales1, e2_own, nranks: int, rank: int,
 
 
 def call(nranks: int, rank: int, x, m_fast, m_slow, recv_codes, recv_scales,
-         gath_codes, gath_scales, comp: bool = True, bits: int = 4):
+         gath_codes, gath_scales, comp: bool = True, bits: int = 4, threads: int = 1, out=None):
     """Rank-mode call. recv_*/gath_* are lists of P arrays (slot `rank` may be
-    None).  Updates m_fast/m_slow in place.  Returns a dict of outputs."""
+    None).  Updates m_fast/m_slow in place.  Returns a dict of outputs.
+
+    threads > 1 runs the threaded driver (orc_call_mt: the same step
+    functions on disjoint runs of groups, bit-identical outputs).  `out`, a
+    dict returned by an earlier call of the same shape, is reused for the
+    outputs instead of fresh arrays."""
     n = x.size
     Cn = n // nranks
-    send_codes = np.zeros(code_bytes(n, bits), np.uint8)
-    send_scales = np.zeros(n // GROUP, np.float32)
-    own_codes2 = np.zeros(code_bytes(Cn, bits), np.uint8)
-    own_scales2 = np.zeros(Cn // GROUP, np.float32)
-    y = np.zeros(n, np.uint16)
-    rc = lib().orc_call(nranks, rank, n, _p(x), _p(m_fast), _p(m_slow),
-                        _ptr_array(recv_codes), _ptr_array(recv_scales),
-                        _ptr_array(gath_codes), _ptr_array(gath_scales),
-                        _p(send_codes), _p(send_scales), _p(own_codes2), _p(own_scales2),
-                        _p(y), int(bool(comp)), bits)
+    if out is None:
+        out = dict(send_codes=np.zeros(code_bytes(n, bits), np.uint8),
+                   send_scales=np.zeros(n // GROUP, np.float32),
+                   own_codes2=np.zeros(code_bytes(Cn, bits), np.uint8),
+                   own_scales2=np.zeros(Cn // GROUP, np.float32),
+                   y=np.zeros(n, np.uint16))
+    send_codes, send_scales = out["send_codes"], out["send_scales"]
+    own_codes2, own_scales2, y = out["own_codes2"], out["own_scales2"], out["y"]
+    args = (nranks, rank, n, _p(x), _p(m_fast), _p(m_slow),
+            _ptr_array(recv_codes), _ptr_array(recv_scales),
+            _ptr_array(gath_codes), _ptr_array(gath_scales),
+            _p(send_codes), _p(send_scales), _p(own_codes2), _p(own_scales2),
+            _p(y), int(bool(comp)), bits)
+    rc = lib().orc_call_mt(int(threads), *args) if threads > 1 else lib().orc_call(*args)
     if rc != 0:
         raise ValueError("orc_call rejected its arguments")
-    return dict(send_codes=send_codes, send_scales=send_scales, own_codes2=own_codes2,
-                own_scales2=own_scales2, y=y)
+    return out
 
 
 def simulate(xs, m_fast=None, m_slow=None, comp: bool = True, want_detail: bool = False,

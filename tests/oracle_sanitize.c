@@ -70,6 +70,17 @@ static int check(int P, int chunks, int bits, int comp) {
     bad |= orc_call(P, p, n, xs[p], f, s, rc, rs, gc, gs, send_c, send_s, own_c, own_s, y1, comp, bits);
     bad |= memcmp(y1, y, n * sizeof(uint16_t)) != 0;
     if (comp) bad |= memcmp(f, mf[p], n * sizeof(float)) != 0 || memcmp(s, ms[p], n * sizeof(float)) != 0;
+    /* the threaded driver, with more threads than some steps have groups */
+    for (int T = 2; T <= 5; T += 3) {
+      memcpy(f, mf0[p], n * sizeof(float));
+      memcpy(s, ms0[p], n * sizeof(float));
+      memset(y1, 0, n * sizeof(uint16_t));
+      bad |= orc_call_mt(T, P, p, n, xs[p], f, s, rc, rs, gc, gs, send_c, send_s, own_c, own_s, y1,
+                         comp, bits);
+      bad |= memcmp(y1, y, n * sizeof(uint16_t)) != 0;
+      if (comp)
+        bad |= memcmp(f, mf[p], n * sizeof(float)) != 0 || memcmp(s, ms[p], n * sizeof(float)) != 0;
+    }
     memcpy(f, mf0[p], n * sizeof(float));
     memcpy(s, ms0[p], n * sizeof(float));
     bad |= orc_rs_call(P, p, n, xs[p], f, s, rc, rs, send_c, send_s, y_own, comp, bits);
