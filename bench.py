@@ -118,13 +118,24 @@ def host_cpu() -> str:
                     break
     except OSError:
         pass
-    return f"{model}, {os.cpu_count()} logical CPUs visible"
+    return (f"{model}, {os.cpu_count()} logical CPUs visible, "
+            f"{len(os.sched_getaffinity(0))} usable by this process")
+
+
+def oracle_threads() -> int:
+    """Host threads for the oracle's all-core leg: the CPUs this process may
+    run on, at most 16 (one GPU's share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def cpu_baseline(x, recv, gath, P: int, rank: int, n_sample: int, calls: int):
-    """The CPU oracle as it stands (one thread), rank-mode calls on the first
-    n_sample elements of the same workload (the sample's chunks are prefixes
-    of the workload's shards), the averages carried; payload GB/s."""
+    """The CPU oracle as it stands, rank-mode calls on the first n_sample
+    elements of the workload (the whole workload by default; a smaller
+    sample's chunks are prefixes of the workload's shards), from zero state:
+    one call on one thread, then `calls` calls on all host cores through the
+    oracle's threaded driver (the single-thread step functions over disjoint
+    runs of groups), state carried.  The first all-core call must give the
+    single-thread call's bytes.  Payload GB/s of each."""
     import numpy as np
 
     from oracle import oracle as orc
@@ -135,19 +146,35 @@ def cpu_baseline(x, recv, gath, P: int, rank: int, n_sample: int, calls: int):
     rs = [None if m is None else np.ascontiguousarray(m[1][:Cs // 128]) for m in recv]
     gc = [None if m is None else np.ascontiguousarray(m[0][:Cs // 2]) for m in gath]
     gs = [None if m is None else np.ascontiguousarray(m[1][:Cs // 128]) for m in gath]
-    mf = np.zeros(n_sample, np.float32)
-    ms = np.zeros(n_sample, np.float32)
+    T = oracle_threads()
+    mf, ms = np.zeros(n_sample, np.float32), np.zeros(n_sample, np.float32)
     t0 = time.perf_counter()
-    for _ in range(calls):
-        orc.call(P, rank, xs, mf, ms, rc, rs, gc, gs)
-    dt = time.perf_counter() - t0
+    one = orc.call(P, rank, xs, mf, ms, rc, rs, gc, gs, threads=1)
+    dt1 = time.perf_counter() - t0
+    mf[:] = 0.0
+    ms[:] = 0.0
+    out, dtT = None, []
+    for k in range(max(1, calls)):
+        t0 = time.perf_counter()
+        out = orc.call(P, rank, xs, mf, ms, rc, rs, gc, gs, threads=T, out=out)
+        dtT.append(time.perf_counter() - t0)
+        if k == 0:
+            same = all(np.array_equal(out[key], one[key]) for key in one)
+            del one
+    gbps = lambda dt: round(2.0 * n_sample / dt / 1e9, 4)  # noqa: E731
+    mean_T = float(np.mean(dtT))
     return {
-        "value": round(2.0 * n_sample * calls / dt / 1e9, 4),
+        "value": gbps(mean_T),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": T,
         "kind": "oracle",
-        "sample": (f"{calls} rank-mode calls (P={P}, rank {rank}) on the first {n_sample} "
-                   f"elements of the workload, averages carried; {dt:.1f} s on 1 thread"),
+        "sample": (f"rank-mode calls (P={P}, rank {rank}) on {n_sample} elements"
+                   f"{' (the whole workload)' if n_sample == x.size else ''} from zero state: "
+                   f"1 call on 1 thread ({dt1:.2f} s), then {len(dtT)} calls on {T} threads, "
+                   f"state carried ({sum(dtT):.2f} s)"),
+        "single_thread": {"GBps": gbps(dt1), "s_per_call": round(dt1, 3)},
+        "all_cores": {"GBps": gbps(mean_T), "s_per_call": round(mean_T, 3), "threads": T},
+        "all_core_output_equals_single_thread": bool(same),
         "host": host_cpu(),
     }
 
@@ -539,34 +566,43 @@ def run_workload(args) -> int:
 
 
 def workload_cpu_baseline(xs, recv_h, gath_h, P: int, rank: int, nstates: int, budget_s: float):
-    """The CPU oracle as it stands (one thread) on the workload's own call
-    sequence: the step's calls in order, from zero state (one state per
-    direction for the training step), until the step ends or about
-    budget_s seconds have passed; payload GB/s."""
+    """The CPU oracle as it stands on the workload's own call sequence, from
+    zero state (one state per direction for the training step): the first
+    call on one thread, then the step's calls in order on all host cores
+    (the oracle's threaded driver) until the step ends or about budget_s
+    seconds have passed; payload GB/s of each."""
     import numpy as np
 
     from oracle import oracle as orc
 
     n = int(xs[0].numel())
     calls = len(xs)
+    T = oracle_threads()
     sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
     rc, rs, gc, gs = sl(recv_h, 0), sl(recv_h, 1), sl(gath_h, 0), sl(gath_h, 1)
+    x0 = xs[0].cpu().numpy().view(np.uint16)
+    mf, ms = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    t0 = time.perf_counter()
+    orc.call(P, rank, x0, mf, ms, rc, rs, gc, gs, threads=1)
+    dt1 = time.perf_counter() - t0
     states = [(np.zeros(n, np.float32), np.zeros(n, np.float32)) for _ in range(nstates)]
-    done, spent = 0, 0.0
-    while done < calls and spent < budget_s:
+    done, spent, out = 0, 0.0, None
+    while done < calls and (done == 0 or spent < budget_s):
         x = xs[done].cpu().numpy().view(np.uint16)
         mf, ms = states[0] if nstates == 1 or done < calls // nstates else states[1]
         t0 = time.perf_counter()
-        orc.call(P, rank, x, mf, ms, rc, rs, gc, gs)
+        out = orc.call(P, rank, x, mf, ms, rc, rs, gc, gs, threads=T, out=out)
         spent += time.perf_counter() - t0
         done += 1
     return {
         "value": round(2.0 * n * done / spent / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": T,
         "kind": "oracle",
-        "sample": f"the first {done} of the step's {calls} rank-mode calls (P={P}, rank {rank}), "
-                  f"{n} elements each, state carried; {spent:.2f} s on one host thread",
+        "sample": f"the step's first call on 1 thread ({dt1:.3f} s), then its first {done} of "
+                  f"{calls} rank-mode calls (P={P}, rank {rank}), {n} elements each, state carried, "
+                  f"on {T} threads ({spent:.2f} s)",
+        "single_thread": {"GBps": round(2.0 * n / dt1 / 1e9, 4), "s_per_call": round(dt1, 4)},
         "host": host_cpu(),
     }
 
@@ -579,8 +615,9 @@ def main() -> int:
     ap.add_argument("--log2n", type=int, default=29, help="elements per rank = 2^log2n")
     ap.add_argument("--nranks", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-log2n", type=int, default=26)
-    ap.add_argument("--cpu-calls", type=int, default=24)
+    ap.add_argument("--cpu-log2n", type=int, default=29,
+                    help="oracle leg: elements of the sample = 2^cpu_log2n (capped at the workload)")
+    ap.add_argument("--cpu-calls", type=int, default=3, help="oracle leg: calls on all host cores")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="smaller workloads: CPU time budget of the oracle leg")
     ap.add_argument("--no-schedules", action="store_true",

@@ -155,6 +155,12 @@ int orc_call_mt(int threads, int nranks, int rank, int64_t n, const uint16_t* x,
                 uint8_t* send_codes, float* send_scales, uint8_t* own_codes2,
                 float* own_scales2, uint16_t* y, int comp, int bits);
 
+/* orc_rs_call split the same way (bit-identical for any thread count). */
+int orc_rs_call_mt(int threads, int nranks, int rank, int64_t n, const uint16_t* x,
+                   float* m_fast, float* m_slow, const uint8_t* const* recv_codes,
+                   const float* const* recv_scales, uint8_t* send_codes, float* send_scales,
+                   uint16_t* y_own, int comp, int bits);
+
 #ifdef __cplusplus
 }
 #endif

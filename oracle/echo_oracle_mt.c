@@ -40,7 +40,7 @@ typedef struct {
   float* e2;       /* own chunk */
   uint8_t* own_codes2;
   float* own_scales2;
-  uint16_t* y;
+  uint16_t* y;     /* all n elements (all-reduce) or the own chunk (reduce-scatter) */
 } call_job;
 
 typedef void (*step_fn)(const call_job* j, int64_t g0, int64_t g1);
@@ -72,6 +72,26 @@ static void step_reduce(const call_job* j, int64_t g0, int64_t g1) {
   }
   orc_reduce_chunk(j->nranks, (g1 - g0) * ORC_GROUP, sc, ss, j->own_codes2 + cb0,
                    j->own_scales2 + g0, j->y + own + e0, j->e2 + e0, j->bits);
+}
+
+/* reduce-scatter: rank-order sum of groups [g0, g1) of the own chunk,
+ * output as bf16 into the chunk-local y */
+static void step_reduce_sum(const call_job* j, int64_t g0, int64_t g1) {
+  const int64_t e0 = g0 * ORC_GROUP;
+  const int64_t cb0 = code_bytes_of(e0, j->bits);
+  const int64_t own = (int64_t)j->rank * j->C;
+  const uint8_t* sc[ORC_MAX_RANKS];
+  const float* ss[ORC_MAX_RANKS];
+  for (int q = 0; q < j->nranks; ++q) {
+    if (q == j->rank) {
+      sc[q] = j->codes1 + code_bytes_of(own, j->bits) + cb0;
+      ss[q] = j->scales1 + own / ORC_GROUP + g0;
+    } else {
+      sc[q] = j->recv_codes[q] + cb0;
+      ss[q] = j->recv_scales[q] + g0;
+    }
+  }
+  orc_reduce_chunk_sum(j->nranks, (g1 - g0) * ORC_GROUP, sc, ss, j->y + e0, j->e2 + e0, j->bits);
 }
 
 /* exit pass over groups [g0, g1) of the gathered chunks, counted over the
@@ -135,51 +155,88 @@ static void parallel_groups(int threads, int64_t groups, step_fn fn, const call_
   }
 }
 
+/* the shared set-up of both threaded calls: checks, the job, its buffers */
+static int job_init(call_job* j, int nranks, int rank, int64_t n, const uint16_t* x,
+                    float* m_fast, float* m_slow, const uint8_t* const* recv_codes,
+                    const float* const* recv_scales, uint16_t* y, int comp, int bits) {
+  if (nranks < 1 || nranks > ORC_MAX_RANKS || rank < 0 || rank >= nranks) return -1;
+  if (n <= 0 || n % ((int64_t)nranks * ORC_GROUP) != 0 || (bits != 4 && bits != 8)) return -1;
+  memset(j, 0, sizeof *j);
+  j->nranks = nranks;
+  j->rank = rank;
+  j->comp = comp;
+  j->bits = bits;
+  j->n = n;
+  j->C = n / nranks;
+  j->x = x;
+  j->m_fast = m_fast;
+  j->m_slow = m_slow;
+  j->recv_codes = recv_codes;
+  j->recv_scales = recv_scales;
+  j->y = y;
+  j->codes1 = malloc((size_t)code_bytes_of(n, bits));
+  j->scales1 = malloc((size_t)(n / ORC_GROUP) * sizeof(float));
+  j->e2 = malloc((size_t)j->C * sizeof(float));
+  if (!j->codes1 || !j->scales1 || !j->e2) {
+    free(j->codes1); free(j->scales1); free(j->e2);
+    return -1;
+  }
+  return 0;
+}
+
+static void job_free(call_job* j) {
+  free(j->codes1); free(j->scales1); free(j->e2);
+}
+
+static int clamp_threads(int threads) {
+  if (threads < 1) return 1;
+  return threads > MT_MAX_THREADS ? MT_MAX_THREADS : threads;
+}
+
+/* the entry pass, and the stage-1 message of every chunk but the own one */
+static void entry_and_send(int threads, const call_job* j, uint8_t* send_codes, float* send_scales) {
+  const int64_t cg = j->C / ORC_GROUP, cb = code_bytes_of(j->C, j->bits);
+  parallel_groups(threads, j->n / ORC_GROUP, step_encode, j);
+  for (int c = 0; c < j->nranks; ++c) {
+    if (c == j->rank) continue;
+    memcpy(send_codes + c * cb, j->codes1 + c * cb, (size_t)cb);
+    memcpy(send_scales + c * cg, j->scales1 + c * cg, (size_t)cg * sizeof(float));
+  }
+}
+
 int orc_call_mt(int threads, int nranks, int rank, int64_t n, const uint16_t* x, float* m_fast,
                 float* m_slow, const uint8_t* const* recv_codes, const float* const* recv_scales,
                 const uint8_t* const* gath_codes, const float* const* gath_scales,
                 uint8_t* send_codes, float* send_scales, uint8_t* own_codes2,
                 float* own_scales2, uint16_t* y, int comp, int bits) {
-  if (nranks < 1 || nranks > ORC_MAX_RANKS || rank < 0 || rank >= nranks) return -1;
-  if (n <= 0 || n % ((int64_t)nranks * ORC_GROUP) != 0 || (bits != 4 && bits != 8)) return -1;
-  if (threads < 1) threads = 1;
-  if (threads > MT_MAX_THREADS) threads = MT_MAX_THREADS;
   call_job j;
-  memset(&j, 0, sizeof j);
-  j.nranks = nranks;
-  j.rank = rank;
-  j.comp = comp;
-  j.bits = bits;
-  j.n = n;
-  j.C = n / nranks;
-  j.x = x;
-  j.m_fast = m_fast;
-  j.m_slow = m_slow;
-  j.recv_codes = recv_codes;
-  j.recv_scales = recv_scales;
+  if (job_init(&j, nranks, rank, n, x, m_fast, m_slow, recv_codes, recv_scales, y, comp, bits))
+    return -1;
+  threads = clamp_threads(threads);
   j.gath_codes = gath_codes;
   j.gath_scales = gath_scales;
   j.own_codes2 = own_codes2;
   j.own_scales2 = own_scales2;
-  j.y = y;
-  j.codes1 = malloc((size_t)code_bytes_of(n, bits));
-  j.scales1 = malloc((size_t)(n / ORC_GROUP) * sizeof(float));
-  j.e2 = malloc((size_t)j.C * sizeof(float));
-  if (!j.codes1 || !j.scales1 || !j.e2) {
-    free(j.codes1); free(j.scales1); free(j.e2);
-    return -1;
-  }
-  const int64_t groups = n / ORC_GROUP, cg = j.C / ORC_GROUP;
-  const int64_t cb = code_bytes_of(j.C, bits);
-  parallel_groups(threads, groups, step_encode, &j);
-  for (int c = 0; c < nranks; ++c) {
-    if (c == rank) continue;
-    memcpy(send_codes + c * cb, j.codes1 + c * cb, (size_t)cb);
-    memcpy(send_scales + c * cg, j.scales1 + c * cg, (size_t)cg * sizeof(float));
-  }
+  const int64_t cg = j.C / ORC_GROUP;
+  entry_and_send(threads, &j, send_codes, send_scales);
   parallel_groups(threads, cg, step_reduce, &j);
   parallel_groups(threads, (int64_t)(nranks - 1) * cg, step_decode, &j);
-  if (comp) parallel_groups(threads, groups, step_update, &j);
-  free(j.codes1); free(j.scales1); free(j.e2);
+  if (comp) parallel_groups(threads, n / ORC_GROUP, step_update, &j);
+  job_free(&j);
+  return 0;
+}
+
+int orc_rs_call_mt(int threads, int nranks, int rank, int64_t n, const uint16_t* x,
+                   float* m_fast, float* m_slow, const uint8_t* const* recv_codes,
+                   const float* const* recv_scales, uint8_t* send_codes, float* send_scales,
+                   uint16_t* y_own, int comp, int bits) {
+  call_job j;
+  if (job_init(&j, nranks, rank, n, x, m_fast, m_slow, recv_codes, recv_scales, y_own, comp, bits))
+    return -1;
+  threads = clamp_threads(threads);
+  entry_and_send(threads, &j, send_codes, send_scales);
+  parallel_groups(threads, j.C / ORC_GROUP, step_reduce_sum, &j);
+  if (comp) parallel_groups(threads, n / ORC_GROUP, step_update, &j);
+  job_free(&j);
   return 0;
 }

@@ -62,6 +62,8 @@ def _load():
                                _vp, _vp, _vp, _vp, _vp, C.c_int, C.c_int]),
         "orc_call_mt": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, C.c_int]),
+        "orc_rs_call_mt": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _vp, _vp, C.c_int, C.c_int]),
         "orc_update_span": (None, [C.c_int64, C.c_int64, C.c_int64, C.c_int64, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, C.c_int]),
         "orc_simulate": (C.c_int, [C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -291,16 +293,18 @@ def reduce_chunk_sum(shard_codes, shard_scales, chunk_n: int, bits: int = 4):
 
 
 def rs_call(nranks: int, rank: int, x, m_fast, m_slow, recv_codes, recv_scales, comp: bool = True,
-            bits: int = 4):
-    """Rank-mode reduce-scatter call.  Returns dict(send_codes, send_scales, y_own)."""
+            bits: int = 4, threads: int = 1):
+    """Rank-mode reduce-scatter call.  Returns dict(send_codes, send_scales, y_own).
+    threads > 1 runs the threaded driver (bit-identical outputs)."""
     n = x.size
     Cn = n // nranks
     send_codes = np.zeros(code_bytes(n, bits), np.uint8)
     send_scales = np.zeros(n // GROUP, np.float32)
     y_own = np.zeros(Cn, np.uint16)
-    rc = lib().orc_rs_call(nranks, rank, n, _p(x), _p(m_fast), _p(m_slow), _ptr_array(recv_codes),
-                           _ptr_array(recv_scales), _p(send_codes), _p(send_scales), _p(y_own),
-                           int(bool(comp)), bits)
+    args = (nranks, rank, n, _p(x), _p(m_fast), _p(m_slow), _ptr_array(recv_codes),
+            _ptr_array(recv_scales), _p(send_codes), _p(send_scales), _p(y_own),
+            int(bool(comp)), bits)
+    rc = lib().orc_rs_call_mt(int(threads), *args) if threads > 1 else lib().orc_rs_call(*args)
     if rc != 0:
         raise ValueError("orc_rs_call rejected its arguments")
     return dict(send_codes=send_codes, send_scales=send_scales, y_own=y_own)

@@ -84,6 +84,17 @@ static int check(int P, int chunks, int bits, int comp) {
     memcpy(f, mf0[p], n * sizeof(float));
     memcpy(s, ms0[p], n * sizeof(float));
     bad |= orc_rs_call(P, p, n, xs[p], f, s, rc, rs, send_c, send_s, y_own, comp, bits);
+    {
+      float* f2 = malloc(n * sizeof(float));
+      float* s2 = malloc(n * sizeof(float));
+      uint16_t* y2 = malloc(C * sizeof(uint16_t));
+      memcpy(f2, mf0[p], n * sizeof(float));
+      memcpy(s2, ms0[p], n * sizeof(float));
+      bad |= orc_rs_call_mt(3, P, p, n, xs[p], f2, s2, rc, rs, send_c, send_s, y2, comp, bits);
+      bad |= memcmp(y2, y_own, C * sizeof(uint16_t)) != 0;
+      bad |= memcmp(f2, f, n * sizeof(float)) != 0 || memcmp(s2, s, n * sizeof(float)) != 0;
+      free(f2); free(s2); free(y2);
+    }
     free(f);
     free(s);
   }

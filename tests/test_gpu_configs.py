@@ -9,14 +9,22 @@ the launch configuration bench.py times.
   prefill  rank mode, [8192 x 4096] (32M elements), 4 warm-up calls then the
            measured call; sampled windows of every chunk checked after every
            call (the oracle follows each window through the whole sequence),
-           the exit pass checked in full.
+           and every output byte of the measured call against the oracle's
+           own run of the whole sequence.
   train    rank mode, [8 x 4096 x 1024], 56 forward calls on one state then 56
            backward calls on another, inputs drawn on the GPU each call;
-           sampled windows after every call.
+           sampled windows after every call, every output byte of the last
+           forward and the last backward call.
   1gb      rank mode, bf16[2^29], 23 calls on the same input (the bench's 3
-           warm-up + 20 timed); sampled windows after every call, the first
-           call's whole send message and the whole exit pass checked in full.
+           warm-up + 20 timed); sampled windows after every call, every
+           output byte of calls 0 and 22.
+The whole-tensor oracle runs are the oracle's threaded driver (the
+single-thread step functions over disjoint runs of groups, pinned
+bit-identical to the single-thread call on the CPU), from zero state, on the
+same inputs: no oracle input comes from the GPU.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -75,13 +83,59 @@ def test_config_decode_full_simulation():
 
 # ---- rank mode --------------------------------------------------------------------------
 
+# host threads for the whole-tensor oracle runs (the CPU share of one GPU)
+ORACLE_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+class FullOracle:
+    """The oracle's run of a rank-mode call sequence on the whole tensor, from
+    zero state, with the sequence's own seeded messages and inputs."""
+
+    def __init__(self, run):
+        self.run = run
+        self.mf = np.zeros(run.n, np.float32)
+        self.ms = np.zeros(run.n, np.float32)
+        sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
+        self.msgs = (sl(run.recv, 0), sl(run.recv, 1), sl(run.gath, 0), sl(run.gath, 1))
+        self.out = None
+
+    def call(self, x_host):
+        r = self.run
+        self.out = orc.call(r.P, r.rank, x_host, self.mf, self.ms, *self.msgs, comp=r.comp,
+                            bits=r.bits, threads=ORACLE_THREADS, out=self.out)
+
+    def compare(self, tag):
+        """every byte of the GPU's outputs and averages against this run's"""
+        torch.cuda.synchronize()
+        r, want = self.run, self.out
+        C, p, f = r.C, r.rank, r.f
+        what = f"{r.label} {tag} (whole tensor)"
+        g.eq(g.host(r.y, np.uint16), want["y"], what + " y")
+        g.eq(g.host(r.own_c, np.uint8), want["own_codes2"], what + " own codes2")
+        g.eq(g.host(r.own_s, np.float32), want["own_scales2"], what + " own scales2")
+        sc, ss = g.host(r.send_c, np.uint8), g.host(r.send_s, np.float32)
+        for j in range(r.P):
+            if j == p:
+                continue  # the own chunk of the send message is not written
+            cs, gs = slice(j * C // f, (j + 1) * C // f), slice(j * C // 128, (j + 1) * C // 128)
+            g.eq(sc[cs], want["send_codes"][cs], what + f" send codes chunk {j}")
+            g.eq(ss[gs], want["send_scales"][gs], what + f" send scales chunk {j}")
+        del sc, ss
+        if r.comp:
+            g.eq(g.host(r.mf, np.float32), self.mf, what + " m_fast")
+            g.eq(g.host(r.ms, np.float32), self.ms, what + " m_slow")
+        say(f"{what}: every byte equal")
+
+
 class RankRun:
     """Device buffers of one rank-mode sequence plus the oracle's windows."""
 
-    def __init__(self, P, rank, n, seed, windows_per_chunk=2, W=4, label="", bits=4, comp=True):
+    def __init__(self, P, rank, n, seed, windows_per_chunk=2, W=4, label="", bits=4, comp=True,
+                 full=False):
         self.P, self.rank, self.n, self.C = P, rank, n, n // P
         self.label = label
         self.bits = bits
+        self.comp = comp
         self.f = 1 if bits == 8 else 2  # elements per code byte
         C = self.C
         self.recv = [None if q == rank else I.int4_message(C, I.stream_key(label, seed, "recv", q),
@@ -105,6 +159,11 @@ class RankRun:
         rng = np.random.default_rng(seed)
         self.wins = [g.WindowOracle(P, rank, j, off, W, bits=bits, comp=comp)
                      for j, off in g.pick_windows(P, C, W, rng, windows_per_chunk)]
+        self.full = FullOracle(self) if full else None
+
+    def oracle_call(self, x_host):
+        """advance the whole-tensor oracle by one call on the same input"""
+        self.full.call(x_host)
 
     def call(self, xd):
         sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
@@ -163,19 +222,6 @@ class RankRun:
                 g.eq(g.host(self.send_s[es.start // 128:es.stop // 128], np.float32), want["scales"],
                      what + " send scales")
 
-    def check_exit_full(self, tag):
-        """The whole exit pass: y on every non-own chunk against the oracle's
-        decode of the gathered chunk; the own chunk's y against the decode of
-        the own stage-2 chunk."""
-        torch.cuda.synchronize()
-        C, r = self.C, self.rank
-        y = g.host(self.y, np.uint16)
-        for j in range(self.P):
-            want = (orc.decode(g.host(self.own_c, np.uint8), g.host(self.own_s, np.float32), C,
-                               bits=self.bits)
-                    if j == r else orc.decode(self.gath[j][0], self.gath[j][1], C, bits=self.bits))
-            g.eq(y[j * C:(j + 1) * C], want, f"{self.label} {tag} y chunk {j}")
-
     def check_message_properties(self, tag):
         """Send and own stage-2 messages never hold the code -8 and their scales
         are finite and non-negative."""
@@ -201,15 +247,16 @@ class RankRun:
 def test_config_prefill_rank_mode():
     P, rank, tokens, hidden = 8, 0, 8192, 4096
     n = tokens * hidden
-    run = RankRun(P, rank, n, seed=3, label="prefill")
+    run = RankRun(P, rank, n, seed=3, label="prefill", full=True)
     ck = I.stream_key("prefill", "channels")
     for call in range(5):  # 4 warm-up calls, then the measured call on warm state
         x = I.lognormal_channel_activations(tokens, hidden, I.stream_key("prefill", call), ck)
         xd = g.dev(x)
         run.call(xd)
+        run.oracle_call(x)
         run.check_windows(xd, f"call {call}")
         say(f"prefill: call {call} windows ok")
-    run.check_exit_full("final call")
+    run.full.compare("measured call 4")
     run.check_message_properties("final call")
 
 
@@ -222,23 +269,26 @@ def test_config_train_rank_mode():
     n = b * s * hidden
     dev = torch.device(g.DEV)
     lam = I.channel_scales(hidden, I.stream_key("train", "channels"))
-    fwd = RankRun(P, rank, n, seed=41, windows_per_chunk=1, label="train-fwd")
-    bwd = RankRun(P, rank, n, seed=43, windows_per_chunk=1, label="train-bwd")
+    fwd = RankRun(P, rank, n, seed=41, windows_per_chunk=1, label="train-fwd", full=True)
+    bwd = RankRun(P, rank, n, seed=43, windows_per_chunk=1, label="train-bwd", full=True)
     for site in range(56):
         xd = I.device_lognormal_channel_activations(b * s, hidden, 1000 + site, lam, dev)
         fwd.call(xd)
+        fwd.oracle_call(g.host(xd, np.uint16))
         fwd.check_windows(xd, f"forward site {site}")
         if site % 14 == 0:
             say(f"train: forward site {site} ok")
+    fwd.full.compare("last forward call")
     for site in reversed(range(56)):
         xd = I.device_student_t3(n, 2000 + site, dev)
         bwd.call(xd)
+        bwd.oracle_call(g.host(xd, np.uint16))
         bwd.check_windows(xd, f"backward site {site}")
         if site % 14 == 0:
             say(f"train: backward site {site} ok")
+    bwd.full.compare("last backward call")
     fwd.check_message_properties("last forward call")
     bwd.check_message_properties("last backward call")
-    bwd.check_exit_full("last backward call")
 
 
 @pytest.mark.timeout(900)
@@ -250,26 +300,15 @@ def test_config_1gb_rank_mode():
     say("1gb: generating inputs")
     x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 0, "x"), outlier_mult=20.0)
     xd = g.dev(x)
-    run = RankRun(P, rank, n, seed=0, windows_per_chunk=3, label="1gb")
+    run = RankRun(P, rank, n, seed=0, windows_per_chunk=3, label="1gb", full=True)
     for call in range(23):
         run.call(xd)
-        if call == 0:
-            # whole send message of the first call (zero state) against the oracle
-            torch.cuda.synchronize()
-            zeros = np.zeros(C, np.float32)
-            sc = g.host(run.send_c, np.uint8)
-            ss = g.host(run.send_s, np.float32)
-            for j in range(P):
-                if j == rank:
-                    continue
-                wc, ws = orc.encode(np.ascontiguousarray(x[j * C:(j + 1) * C]), zeros, zeros)
-                g.eq(sc[j * C // 2:(j + 1) * C // 2], wc, f"1gb call 0 send codes chunk {j}")
-                g.eq(ss[j * C // 128:(j + 1) * C // 128], ws, f"1gb call 0 send scales chunk {j}")
-            say("1gb: call 0 whole send message ok")
+        run.oracle_call(x)
+        if call in (0, 22):
+            run.full.compare(f"call {call}")
         run.check_windows(xd, f"call {call}")
         if call % 5 == 0:
             say(f"1gb: call {call} windows ok")
-    run.check_exit_full("call 22")
     run.check_message_properties("call 22")
 
 
@@ -277,17 +316,18 @@ def test_config_1gb_rank_mode():
 def test_1gb_message_sixteen_ranks():
     """The 1 GB message at the largest rank count (P = 16, rank 11): 15
     incoming shards per chunk element, four calls with the averages carried,
-    windows of every chunk, the whole exit pass."""
+    windows of every chunk after each call, every output byte of the last."""
     P, rank, n = 16, 11, 1 << 29
     say("1gb P=16: generating inputs")
     x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 16, "x"), outlier_mult=20.0)
     xd = g.dev(x)
-    run = RankRun(P, rank, n, seed=16, windows_per_chunk=2, label="1gb P=16")
+    run = RankRun(P, rank, n, seed=16, windows_per_chunk=2, label="1gb P=16", full=True)
     for call in range(4):
         run.call(xd)
+        run.oracle_call(x)
         run.check_windows(xd, f"call {call}")
         say(f"1gb P=16: call {call} windows ok")
-    run.check_exit_full("call 3")
+    run.full.compare("call 3")
     run.check_message_properties("call 3")
 
 
@@ -295,17 +335,19 @@ def test_1gb_message_sixteen_ranks():
 def test_1gb_message_8bit_promoted_call():
     """The 1 GB message with 8-bit codes (the promoted width), as the bench
     times it: P = 8, rank 0, four calls with the averages carried, windows
-    of every chunk, the whole exit pass, no -128 code in any message."""
+    of every chunk after each call, every output byte of the last, no -128
+    code in any message."""
     P, rank, n = 8, 0, 1 << 29
     say("1gb 8-bit: generating inputs")
     x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 8, "x"), outlier_mult=20.0)
     xd = g.dev(x)
-    run = RankRun(P, rank, n, seed=8, windows_per_chunk=2, label="1gb 8-bit", bits=8)
+    run = RankRun(P, rank, n, seed=8, windows_per_chunk=2, label="1gb 8-bit", bits=8, full=True)
     for call in range(4):
         run.call(xd)
+        run.oracle_call(x)
         run.check_windows(xd, f"call {call}")
         say(f"1gb 8-bit: call {call} windows ok")
-    run.check_exit_full("call 3")
+    run.full.compare("call 3")
     run.check_message_properties("call 3")
 
 
@@ -313,7 +355,8 @@ def test_1gb_message_8bit_promoted_call():
 def test_1gb_message_reduce_scatter():
     """The reduce-scatter call at the bench's size (bf16[2^29], P = 8, rank
     0): four calls with the averages carried, windows of every chunk (send
-    codes or y_own, and the averages) against the oracle."""
+    codes or y_own, and the averages) after each call and every output byte
+    of the last against the oracle."""
     P, rank, n = 8, 0, 1 << 29
     C = n // P
     say("1gb reduce-scatter: generating inputs")
@@ -328,8 +371,11 @@ def test_1gb_message_reduce_scatter():
     send_c, send_s, y_own = g.empty_u8(n // 2), g.empty_f32(n // 128), g.empty_bf16(C)
     rng = np.random.default_rng(12)
     wins = [g.RSWindowOracle(P, rank, j, off, 4) for j, off in g.pick_windows(P, C, 4, rng, 2)]
+    hmf, hms = np.zeros(n, np.float32), np.zeros(n, np.float32)  # the oracle's whole-tensor run
     for call in range(4):
         B.echo_rs_call(st, xd, rc, rs, send_c, send_s, y_own)
+        want_all = orc.rs_call(P, rank, x, hmf, hms, [None if m is None else m[0] for m in recv],
+                               [None if m is None else m[1] for m in recv], threads=ORACLE_THREADS)
         torch.cuda.synchronize()
         for w in wins:
             es, ce = w.elems(C), w.chunk_elems()
@@ -346,6 +392,17 @@ def test_1gb_message_reduce_scatter():
                 g.eq(g.host(send_s[es.start // 128:es.stop // 128], np.float32), want["scales"],
                      what + " send scales")
         say(f"1gb reduce-scatter: call {call} windows ok")
+    what = "1gb rs call 3 (whole tensor)"
+    g.eq(g.host(y_own, np.uint16), want_all["y_own"], what + " y_own")
+    keep = np.ones(n // 2, bool)
+    keep[rank * C // 2:(rank + 1) * C // 2] = False
+    g.eq(g.host(send_c, np.uint8)[keep], want_all["send_codes"][keep], what + " send codes")
+    keep_s = np.ones(n // 128, bool)
+    keep_s[rank * C // 128:(rank + 1) * C // 128] = False
+    g.eq(g.host(send_s, np.float32)[keep_s], want_all["send_scales"][keep_s], what + " send scales")
+    g.eq(g.host(mf, np.float32), hmf, what + " m_fast")
+    g.eq(g.host(ms, np.float32), hms, what + " m_slow")
+    say(f"{what}: every byte equal")
 
 
 @pytest.mark.timeout(900)
@@ -353,13 +410,14 @@ def test_1gb_message_reduce_scatter():
 def test_1gb_message_other_schedules(schedule):
     """The bench's other 1 GB schedules: the uncompensated call, and the
     split schedule (averages read-only on the critical path, the update on a
-    side stream); four calls, windows of every chunk against the oracle."""
+    side stream); four calls, windows of every chunk after each call and
+    every output byte of the last against the oracle."""
     P, rank, n = 8, 0, 1 << 29
     say(f"1gb {schedule}: generating inputs")
     x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 0, "x"), outlier_mult=20.0)
     xd = g.dev(x)
     run = RankRun(P, rank, n, seed=21, windows_per_chunk=2, label=f"1gb {schedule}",
-                  comp=schedule != "uncompensated")
+                  comp=schedule != "uncompensated", full=True)
     e2 = g.empty_f32(n // P)
     side = torch.cuda.Stream()
     for call in range(4):
@@ -367,9 +425,10 @@ def test_1gb_message_other_schedules(schedule):
             run.call_plain(xd)
         else:
             run.call_split(xd, e2, side)
+        run.oracle_call(x)
         run.check_windows(xd, f"call {call}")
         say(f"1gb {schedule}: call {call} windows ok")
-    run.check_exit_full("call 3")
+    run.full.compare("call 3")
 
 
 @pytest.mark.parametrize("a", [1.0, 1.1])

@@ -1,5 +1,5 @@
-"""The oracle's threaded driver (orc_call_mt) against the single-thread call
-it parallelizes: for every thread count, rank count, rank, code width and
+"""The oracle's threaded driver (orc_call_mt, orc_rs_call_mt) against the
+single-thread call it parallelizes: for every thread count, rank count, rank, code width and
 with or without compensation, a sequence of rank-mode calls gives the same
 bytes -- send message, own stage-2 chunk, y and both averages.  Group counts
 are chosen so that the runs of groups are ragged and some threads get none."""
@@ -59,3 +59,26 @@ def test_threaded_call_rejects_what_the_call_rejects():
         with pytest.raises(ValueError):
             # P = 8 with 1024 elements has one group per chunk; rank 8 is out of range
             orc.call(8, 8, x, mf, ms, none, none, none, none, threads=4, **kw)
+
+
+@pytest.mark.parametrize("threads", [2, 3, 16])
+@pytest.mark.parametrize("P,rank,k", [(1, 0, 5), (3, 2, 7), (8, 5, 1), (16, 11, 2)])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_threaded_reduce_scatter_equals_single_thread(threads, P, rank, k, bits):
+    C = 128 * k
+    n = P * C
+    key = ("mt-rs", P, rank, k, bits)
+    rc, rs, _, _ = _messages(P, rank, C, key, bits)
+    mf1, ms1 = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    mfT, msT = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    for call in range(3):
+        x = I.to_bf16_bits(3.0 * I.normal(n, I.stream_key(*key, "x", call)))
+        want = orc.rs_call(P, rank, x, mf1, ms1, rc, rs, bits=bits)
+        got = orc.rs_call(P, rank, x, mfT, msT, rc, rs, bits=bits, threads=threads)
+        assert np.array_equal(got["y_own"], want["y_own"]), call
+        f = 1 if bits == 8 else 2
+        keep = np.ones(n // f, bool)
+        keep[rank * C // f:(rank + 1) * C // f] = False
+        assert np.array_equal(got["send_codes"][keep], want["send_codes"][keep]), call
+        assert np.array_equal(mfT.view(np.uint32), mf1.view(np.uint32)), ("m_fast", call)
+        assert np.array_equal(msT.view(np.uint32), ms1.view(np.uint32)), ("m_slow", call)
