@@ -162,10 +162,13 @@ static float dequant(const uint8_t* codes, const float* scales, int64_t i, int b
 
 /* ---- compensator ------------------------------------------------------------ */
 
+/* the correction of one element: the weighted sum of its two averages */
+static float correction_of(float mf, float ms) { return (ORC_W_FAST * mf) + (ORC_W_SLOW * ms); }
+
 static float corrected_input(uint16_t x, float mf, float ms, int comp) {
   float xf = orc_bf16_to_f32(x);
   if (!comp) return xf;
-  float corr = (ORC_W_FAST * mf) + (ORC_W_SLOW * ms);
+  float corr = correction_of(mf, ms);
   return xf - corr;
 }
 
@@ -343,6 +346,37 @@ int orc_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const*
   }
   free(e2);
   return ok ? 0 : -1;
+}
+
+/* ---- the correction kept as one array --------------------------------------------
+ * In the pages' schedule the averages' update runs beside the next matrix
+ * multiplication, off the critical path ("Tensor-parallel traffic drops to 4
+ * bits", Interpretation).  Keeping the next call's correction as one array,
+ * written by that update, lets the critical-path entry pass read one value
+ * per element instead of both averages; the values are the same binary32
+ * numbers the entry pass would form from the averages. */
+
+void orc_correction(int64_t n, const float* m_fast, const float* m_slow, float* corr) {
+  for (int64_t i = 0; i < n; ++i) corr[i] = correction_of(m_fast[i], m_slow[i]);
+}
+
+void orc_encode_corr(int64_t n, const uint16_t* x, const float* corr, uint8_t* codes,
+                     float* scales, int bits) {
+  float v[ORC_GROUP];
+  int8_t q[ORC_GROUP];
+  for (int64_t g = 0; g < n / ORC_GROUP; ++g) {
+    int64_t base = g * ORC_GROUP;
+    for (int i = 0; i < ORC_GROUP; ++i) v[i] = orc_bf16_to_f32(x[base + i]) - corr[base + i];
+    orc_quantize_group_q(v, ORC_GROUP, qmax_of(bits), q, &scales[g], 1);
+    orc_pack_codes(q, ORC_GROUP, codes + code_bytes(base, bits), bits);
+  }
+}
+
+void orc_update_corr(int64_t n, int nranks, int rank, const uint16_t* x, float* m_fast,
+                     float* m_slow, const uint8_t* codes1, const float* scales1,
+                     const float* e2_own, float* corr, int bits) {
+  orc_update(n, nranks, rank, x, m_fast, m_slow, codes1, scales1, e2_own, NULL, bits);
+  orc_correction(n, m_fast, m_slow, corr);
 }
 
 /* ---- reduce-scatter only ------------------------------------------------------ */

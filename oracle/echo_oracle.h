@@ -119,6 +119,26 @@ int orc_simulate(int nranks, int64_t n, const uint16_t* const* xs, float* const*
                  uint8_t* const* codes1, float* const* scales1, float* const* xp,
                  float* const* r, int comp, int bits);
 
+/* ---- the correction kept as one array -----------------------------------------
+ * The pages run the averages' update beside the next matrix multiplication,
+ * off the critical path ("Tensor-parallel traffic drops to 4 bits",
+ * Interpretation).  With the next call's correction kept as one array, the
+ * critical-path entry pass reads it instead of both averages. */
+
+/* corr[i] = (W_F m_fast[i]) + (W_S m_slow[i]), the correction the entry pass
+ * subtracts. */
+void orc_correction(int64_t n, const float* m_fast, const float* m_slow, float* corr);
+
+/* Entry pass from a correction array: x' = f32(x) - corr, then group-quantize
+ * x' (stage 1).  Equals orc_encode with the averages corr was formed from. */
+void orc_encode_corr(int64_t n, const uint16_t* x, const float* corr, uint8_t* codes,
+                     float* scales, int bits);
+
+/* orc_update, then corr = the correction of the refreshed averages. */
+void orc_update_corr(int64_t n, int nranks, int rank, const uint16_t* x, float* m_fast,
+                     float* m_slow, const uint8_t* codes1, const float* scales1,
+                     const float* e2_own, float* corr, int bits);
+
 /* ---- reduce-scatter only (the sequence-parallel variant) -------------------
  * The pages name the reduce-scatter of sequence parallelism as a next target
  * ("Tensor-parallel traffic drops to 4 bits", Perspective).  Reading: the

@@ -64,6 +64,10 @@ def _load():
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_int, C.c_int]),
         "orc_rs_call_mt": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _vp, C.c_int, C.c_int]),
+        "orc_correction": (None, [C.c_int64, _vp, _vp, _vp]),
+        "orc_encode_corr": (None, [C.c_int64, _vp, _vp, _vp, _vp, C.c_int]),
+        "orc_update_corr": (None, [C.c_int64, C.c_int, C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   C.c_int]),
         "orc_update_span": (None, [C.c_int64, C.c_int64, C.c_int64, C.c_int64, _vp, _vp, _vp, _vp,
                                    _vp, _vp, _vp, C.c_int]),
         "orc_simulate": (C.c_int, [C.c_int, C.c_int64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -218,6 +222,30 @@ def update(x, m_fast, m_slow, codes1, scales1, e2_own, nranks: int, rank: int,
     lib().orc_update(x.size, nranks, rank, _p(x), _p(m_fast), _p(m_slow), _p(codes1),
                      _p(scales1), _p(e2_own), _p(r), bits)
     return r
+
+
+def correction(m_fast, m_slow) -> np.ndarray:
+    """corr = (W_F m_fast) + (W_S m_slow), elementwise in binary32."""
+    corr = np.zeros(m_fast.size, np.float32)
+    lib().orc_correction(m_fast.size, _p(m_fast), _p(m_slow), _p(corr))
+    return corr
+
+
+def encode_corr(x, corr, bits: int = 4):
+    """Entry pass from a correction array. Returns (codes, scales)."""
+    n = x.size
+    codes = np.zeros(code_bytes(n, bits), np.uint8)
+    scales = np.zeros(n // GROUP, np.float32)
+    lib().orc_encode_corr(n, _p(x), _p(np.ascontiguousarray(corr, np.float32)), _p(codes),
+                          _p(scales), bits)
+    return codes, scales
+
+
+def update_corr(x, m_fast, m_slow, codes1, scales1, e2_own, corr, nranks: int, rank: int,
+                bits: int = 4) -> None:
+    """Refresh the averages in place, then write the next call's correction into corr."""
+    lib().orc_update_corr(x.size, nranks, rank, _p(x), _p(m_fast), _p(m_slow), _p(codes1),
+                          _p(scales1), _p(e2_own), _p(corr), bits)
 
 
 def call(nranks: int, rank: int, x, m_fast, m_slow, recv_codes, recv_scales,
