@@ -263,6 +263,38 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         gemm()
         split_update(reduced)
 
+    corr = torch.empty(N, dtype=torch.float32, device=y.device)
+    B.echo_correction(st, corr, main)
+
+    def split_corr_critical():
+        B.echo_encode_corr(st, xd, corr, send_c, send_s, main)
+        B.echo_reduce_shard(sh_c, sh_s, own_c, own_s, y[rank * C:(rank + 1) * C], e2, chunk_n=C,
+                            stream=main)
+        B.echo_call_exit(st, gc_, gs_, y, main)
+        done = torch.cuda.Event()
+        done.record(main)
+        return done
+
+    def split_corr_update(reduced):
+        side.wait_event(reduced)
+        B.echo_update_corr(st, xd, send_c, send_s, e2, corr, side)
+        ev = torch.cuda.Event()
+        ev.record(side)
+        state["updated"] = ev
+
+    def b_split_corr(e=None):
+        wait_update()  # the entry pass reads the correction the previous update wrote
+        if e: e[0].record(main)
+        reduced = split_corr_critical()
+        if e: e[1].record(main)
+        gemm()
+        split_corr_update(reduced)
+
+    def b_update_corr(e=None):
+        if e: e[0].record(main)
+        B.echo_update_corr(st, xd, send_c, send_s, e2, corr, main)
+        if e: e[1].record(main)
+
     def b_gemm(e=None):
         if e: e[0].record(main)
         gemm()
@@ -310,6 +342,17 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
                        ("update_alone", b_update), ("rs", b_rs), ("call8", b_call8)):
         wall, first = timed(body)
         out[name] = (wall, first)
+        if name == "split":
+            main.wait_event(state["updated"])
+            state["updated"] = None
+    # the correction array must come from the averages the other schedules left
+    B.echo_correction(st, corr, main)
+    for name, body in (("split_corr", b_split_corr), ("update_corr_alone", b_update_corr)):
+        wall, first = timed(body)
+        out[name] = (wall, first)
+        if name == "split_corr":
+            main.wait_event(state["updated"])
+            state["updated"] = None
     torch.cuda.synchronize()
     return {
         "matmul": "[%d x 4096] @ [4096 x 1792] bf16" % (N // 4096),
@@ -318,15 +361,19 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         "plain_call_ms": round(out["plain"][1], 4),
         "split_critical_ms": round(out["split"][1], 4),
         "update_alone_ms": round(out["update_alone"][1], 4),
+        "split_corr_critical_ms": round(out["split_corr"][1], 4),
+        "update_corr_alone_ms": round(out["update_corr_alone"][1], 4),
         "layer_ms": {"fused+matmul": round(out["fused"][0], 4), "plain+matmul": round(out["plain"][0], 4),
-                     "split+matmul(update beside it)": round(out["split"][0], 4)},
+                     "split+matmul(update beside it)": round(out["split"][0], 4),
+                     "split_corr+matmul(update beside it)": round(out["split_corr"][0], 4)},
         "call_8bit_ms": round(out["call8"][1], 4),
         "call_8bit_GBps": round(step_bytes(N, P, bits=8) / (out["call8"][1] * 1e-3) / 1e9, 1),
         "reduce_scatter_call_ms": round(out["rs"][1], 4),
         "reduce_scatter_GBps": round(rs_bytes(N, P) / (out["rs"][1] * 1e-3) / 1e9, 1),
         "compensation_on_critical_path_ms": {
             "fused": round(out["fused"][1] - out["plain"][1], 4),
-            "split": round(out["split"][1] - out["plain"][1], 4)},
+            "split": round(out["split"][1] - out["plain"][1], 4),
+            "split_corr": round(out["split_corr"][1] - out["plain"][1], 4)},
     }
 
 

@@ -52,6 +52,9 @@ _SIGNATURES = {
     "echo_reduce_shard": [C.c_int32, C.c_int64, C.c_int32, _pp, _pp, _vp, _vp, _vp, _vp, _vp],
     "echo_decode": [C.c_int64, C.c_int32, _vp, _vp, _vp, _vp],
     "echo_update": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp, _vp],
+    "echo_correction": [C.POINTER(EchoStateC), _vp, _vp],
+    "echo_encode_corr": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp, _vp],
+    "echo_update_corr": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp, _vp, _vp],
     "echo_call_entry": [C.POINTER(EchoStateC), _vp, _vp, _vp, _vp],
     "echo_call_entry_range": [C.POINTER(EchoStateC), _vp, C.c_int32, C.c_int32, _vp, _vp, _vp],
     "echo_call_reduce": [C.POINTER(EchoStateC), _vp, _pp, _pp, _vp, _vp, _vp, _vp],
@@ -226,6 +229,26 @@ def echo_update(st: EchoState, x, codes1, scales1, e2_own, stream=None) -> None:
     _check(lib.echo_update(C.byref(st.c), _ptr(x, 2 * n, "x"), _ptr(codes1, _cb(n, bits), "codes1"),
                            _ptr(scales1, _sb(n), "scales1"), _ptr(e2_own, 4 * cn, "e2_own"),
                            _stream(stream)), "echo_update")
+
+
+def echo_correction(st: EchoState, corr, stream=None) -> None:
+    n, _, _ = st.sizes()
+    _check(lib.echo_correction(C.byref(st.c), _ptr(corr, 4 * n, "corr"), _stream(stream)),
+           "echo_correction")
+
+
+def echo_encode_corr(st: EchoState, x, corr, codes, scales, stream=None) -> None:
+    n, _, bits = st.sizes()
+    _check(lib.echo_encode_corr(C.byref(st.c), _ptr(x, 2 * n, "x"), _ptr(corr, 4 * n, "corr"),
+                                _ptr(codes, _cb(n, bits), "codes"), _ptr(scales, _sb(n), "scales"),
+                                _stream(stream)), "echo_encode_corr")
+
+
+def echo_update_corr(st: EchoState, x, codes1, scales1, e2_own, corr, stream=None) -> None:
+    n, cn, bits = st.sizes()
+    _check(lib.echo_update_corr(C.byref(st.c), _ptr(x, 2 * n, "x"), _ptr(codes1, _cb(n, bits), "codes1"),
+                                _ptr(scales1, _sb(n), "scales1"), _ptr(e2_own, 4 * cn, "e2_own"),
+                                _ptr(corr, 4 * n, "corr"), _stream(stream)), "echo_update_corr")
 
 
 def echo_call_entry(st: EchoState, x, send_codes, send_scales, stream=None) -> None:

@@ -143,7 +143,7 @@ int launch_stage1(const Stage1Args& a, int bits, hipStream_t s) {
   const uint64_t nslices = ((uint64_t)a.groups_work + 1) / 2;
   if (nslices == 0) return ECHO_SUCCESS;
   const uint32_t blocks =
-      blocks_for((nslices + U - 1) / U, MODE == kUpdate ? (uint32_t)ECHO_UPDATE_MAX_BLOCKS : kMaxBlocks);
+      blocks_for((nslices + U - 1) / U, is_update(MODE) ? (uint32_t)ECHO_UPDATE_MAX_BLOCKS : kMaxBlocks);
   if (bits == 8) return launch(k_stage1<MODE, 8, U>, dim3(blocks), s, a);
   return launch(k_stage1<MODE, 4, U>, dim3(blocks), s, a);
 }
@@ -230,7 +230,7 @@ int run_entry_range(const echo_state* st, const uint16_t* x, int32_t j0, int32_t
   const Geometry g = geometry(st);
   const int32_t r = st->rank;
   const uint32_t chunks = (uint32_t)(j1 - j0) - ((j0 <= r && r < j1) ? 1u : 0u);
-  Stage1Args a;
+  Stage1Args a = {};
   a.x = x;
   a.mf = st->m_fast;
   a.ms = st->m_slow;
@@ -294,8 +294,7 @@ int run_exit(const echo_state* st, const uint8_t* const* gath_codes,
 int run_entry_plain(const echo_state* geo, const uint16_t* x, uint8_t* send_codes,
                     float* send_scales, hipStream_t s) {
   const Geometry g = geometry(geo);
-  Stage1Args a;
-  memset(&a, 0, sizeof a);
+  Stage1Args a = {};
   a.x = x;
   a.codes = send_codes;
   a.scales = send_scales;
@@ -406,7 +405,7 @@ int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* 
   al.in(st->m_fast, n * 4);
   al.in(st->m_slow, n * 4);
   if (!al.ok()) return ECHO_ERR_ALIAS;
-  Stage1Args a;
+  Stage1Args a = {};
   a.x = x;
   a.mf = st->m_fast;
   a.ms = st->m_slow;
@@ -498,7 +497,7 @@ int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
   al.in(scales1, g.n / ECHO_GROUP * 4);
   al.in(e2_own, g.chunk * 4);
   if (!al.ok()) return ECHO_ERR_ALIAS;
-  Stage1Args a;
+  Stage1Args a = {};
   a.x = x;
   a.mf = st->m_fast;
   a.ms = st->m_slow;
@@ -510,6 +509,79 @@ int echo_update(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
   a.own_g0 = g.own_g0;
   a.own_g1 = g.own_g1;
   return launch_stage1<kUpdate>(a, st->bits, (hipStream_t)stream);
+}
+
+int echo_correction(const echo_state* st, float* corr, echo_stream_t stream) {
+  int rc = check_state(st);
+  if (rc) return finished(rc);
+  if (!corr) return ECHO_ERR_INVALID_ARGUMENT;
+  if (!aligned(corr, 16)) return ECHO_ERR_ALIGNMENT;
+  Aliases al;
+  al.out(corr, st->n * 4);
+  al.in(st->m_fast, st->n * 4);
+  al.in(st->m_slow, st->n * 4);
+  if (!al.ok()) return ECHO_ERR_ALIAS;
+  CorrArgs c;
+  c.mf = reinterpret_cast<const float4*>(st->m_fast);
+  c.ms = reinterpret_cast<const float4*>(st->m_slow);
+  c.corr = reinterpret_cast<float4*>(corr);
+  c.n4 = st->n / 4;
+  return launch(k_correction, dim3(blocks_for_items((uint64_t)c.n4)), (hipStream_t)stream, c);
+}
+
+int echo_encode_corr(const echo_state* st, const uint16_t* x, const float* corr, uint8_t* codes,
+                     float* scales, echo_stream_t stream) {
+  int rc = check_state(st);
+  if (rc) return finished(rc);
+  if (!x || !corr || !codes || !scales) return ECHO_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(corr, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return ECHO_ERR_ALIGNMENT;
+  const int64_t n = st->n;
+  Aliases al;
+  al.out(codes, code_bytes(n, st->bits));
+  al.out(scales, n / ECHO_GROUP * 4);
+  al.in(x, n * 2);
+  al.in(corr, n * 4);
+  if (!al.ok()) return ECHO_ERR_ALIAS;
+  Stage1Args a = {};
+  a.x = x;
+  a.corr = const_cast<float*>(corr);
+  a.codes = codes;
+  a.scales = scales;
+  a.groups_work = (uint32_t)(n / ECHO_GROUP);
+  return launch_stage1<kEncodeCorr>(a, st->bits, (hipStream_t)stream);
+}
+
+int echo_update_corr(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
+                     const float* scales1, const float* e2_own, float* corr, echo_stream_t stream) {
+  int rc = check_state(st);
+  if (rc) return finished(rc);
+  if (!x || !codes1 || !scales1 || !e2_own || !corr) return ECHO_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(codes1, 16) || !aligned(scales1, 4) || !aligned(e2_own, 16) ||
+      !aligned(corr, 16))
+    return ECHO_ERR_ALIGNMENT;
+  const Geometry g = geometry(st);
+  Aliases al;
+  al.out(st->m_fast, g.n * 4);
+  al.out(st->m_slow, g.n * 4);
+  al.out(corr, g.n * 4);
+  al.in(x, g.n * 2);
+  al.in(codes1, code_bytes(g.n, st->bits));
+  al.in(scales1, g.n / ECHO_GROUP * 4);
+  al.in(e2_own, g.chunk * 4);
+  if (!al.ok()) return ECHO_ERR_ALIAS;
+  Stage1Args a = {};
+  a.x = x;
+  a.mf = st->m_fast;
+  a.ms = st->m_slow;
+  a.corr = corr;
+  a.codes = const_cast<uint8_t*>(codes1);
+  a.scales = const_cast<float*>(scales1);
+  a.e2 = e2_own;
+  a.groups_work = g.groups;
+  a.own_g0 = g.own_g0;
+  a.own_g1 = g.own_g1;
+  return launch_stage1<kUpdateCorr>(a, st->bits, (hipStream_t)stream);
 }
 
 int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes,

@@ -122,9 +122,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// x' = f32(x) - ((W_F*m_f) + (W_S*m_s))
+// the correction (W_F*m_f) + (W_S*m_s), and x' = f32(x) - correction
+__device__ __forceinline__ float correction(float mf, float ms) {
+  return (ECHO_W_FAST * mf) + (ECHO_W_SLOW * ms);
+}
+
 __device__ __forceinline__ float corrected(float xf, float mf, float ms) {
-  float corr = (ECHO_W_FAST * mf) + (ECHO_W_SLOW * ms);
+  float corr = correction(mf, ms);
   return xf - corr;
 }
 
@@ -202,19 +206,28 @@ __device__ __forceinline__ void refresh(float& mf, float& ms, float r) {
 // ---------------------------------------------------------------------------
 // stage-1 kernel: entry pass / plain encode / plain update / uncompensated entry
 
-enum Stage1Mode { kEncode = 0, kEntryFused = 1, kUpdate = 2, kEntryPlain = 3 };
+// kEncodeCorr / kUpdateCorr: the deferred-update schedule with the next
+// call's correction kept as one array (the entry pass reads it instead of
+// both averages; the update writes it after refreshing them)
+enum Stage1Mode {
+  kEncode = 0, kEntryFused = 1, kUpdate = 2, kEntryPlain = 3, kEncodeCorr = 4, kUpdateCorr = 5
+};
 
 // what each stage-1 mode does
 constexpr bool skips_own(int m) { return m == kEntryFused || m == kEntryPlain; }
-constexpr bool reads_state(int m) { return m != kEntryPlain; }
-constexpr bool writes_state(int m) { return m == kEntryFused || m == kUpdate; }
+constexpr bool reads_state(int m) { return m != kEntryPlain && m != kEncodeCorr; }
+constexpr bool reads_corr(int m) { return m == kEncodeCorr; }
+constexpr bool is_update(int m) { return m == kUpdate || m == kUpdateCorr; }
+constexpr bool writes_state(int m) { return m == kEntryFused || is_update(m); }
+constexpr bool writes_corr(int m) { return m == kUpdateCorr; }
 
 struct Stage1Args {
   const uint16_t* x;      // [n]
   float* mf;              // [n]
   float* ms;              // [n]
-  uint8_t* codes;         // kEncode/kEntryFused: out [n/2]; kUpdate: in
-  float* scales;          // kEncode/kEntryFused: out [n/128]; kUpdate: in
+  float* corr;            // kEncodeCorr: in [n]; kUpdateCorr: out [n]
+  uint8_t* codes;         // encoding modes: out [n/2]; update modes: in
+  float* scales;          // encoding modes: out [n/128]; update modes: in
   const float* e2;        // kUpdate: [own chunk], indexed from own_g0*128
   uint32_t groups_work;   // virtual groups to process
   uint32_t v_base;        // first virtual group (the own chunk is not counted
@@ -264,7 +277,11 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
           f = make_float4(fv.x, fv.y, fv.z, fv.w);
           s = make_float4(sv.x, sv.y, sv.z, sv.w);
         }
-        if (MODE == kUpdate) {
+        if (reads_corr(MODE)) {  // the correction, held where m_f would be
+          const f32x4 cv = ld_stream(reinterpret_cast<const f32x4*>(a.corr + e));
+          f = make_float4(cv.x, cv.y, cv.z, cv.w);
+        }
+        if (is_update(MODE)) {
           cw[u] = load_codes4<BITS>(a.codes, e);
           sc[u] = a.scales[g[u]];
           if (own[u]) {
@@ -283,10 +300,12 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
       float xp[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        xp[k] = reads_state(MODE) ? corrected(xf[u][k], mf[u][k], ms[u][k]) : xf[u][k];
+        xp[k] = reads_state(MODE)  ? corrected(xf[u][k], mf[u][k], ms[u][k])
+                : reads_corr(MODE) ? xf[u][k] - mf[u][k]
+                                   : xf[u][k];
 
       float d1[4];
-      if (MODE == kUpdate) {
+      if (is_update(MODE)) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) d1[k] = (float)code_at<BITS>(cw[u], k) * sc[u];
       } else {
@@ -310,13 +329,17 @@ __global__ __launch_bounds__(kBlock) void k_stage1(Stage1Args a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           float r = d1[k] - xp[k];
-          if (MODE == kUpdate && own[u]) r = r + e2v[u][k];  // e2 only on the own chunk
+          if (is_update(MODE) && own[u]) r = r + e2v[u][k];  // e2 only on the own chunk
           refresh(mf[u][k], ms[u][k], r);
         }
         if (ok[u]) {
           const int64_t e = (int64_t)g[u] * kGroup + sub * 4;
           st_stream(reinterpret_cast<f32x4*>(a.mf + e), f32x4{mf[u][0], mf[u][1], mf[u][2], mf[u][3]});
           st_stream(reinterpret_cast<f32x4*>(a.ms + e), f32x4{ms[u][0], ms[u][1], ms[u][2], ms[u][3]});
+          if (writes_corr(MODE))  // the next call's correction, from the refreshed averages
+            st_stream(reinterpret_cast<f32x4*>(a.corr + e),
+                      f32x4{correction(mf[u][0], ms[u][0]), correction(mf[u][1], ms[u][1]),
+                            correction(mf[u][2], ms[u][2]), correction(mf[u][3], ms[u][3])});
         }
       }
     }
@@ -581,6 +604,24 @@ __global__ __launch_bounds__(kBlock) void k_zero2(Zero2Args z) {
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < z.n4; i += stride) {
     z.a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     z.b[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// corr = (W_F*m_f) + (W_S*m_s) from the current averages (set-up of the
+// deferred-update schedule's correction array)
+struct CorrArgs {
+  const float4* mf;
+  const float4* ms;
+  float4* corr;
+  int64_t n4;  // float4s
+};
+
+__global__ __launch_bounds__(kBlock) void k_correction(CorrArgs c) {
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < c.n4; i += stride) {
+    const float4 f = c.mf[i], s = c.ms[i];
+    c.corr[i] = make_float4(correction(f.x, s.x), correction(f.y, s.y), correction(f.z, s.z),
+                            correction(f.w, s.w));
   }
 }
 

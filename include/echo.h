@@ -93,7 +93,7 @@ extern "C" {
 #define ECHO_ALPHA_SLOW 0.125f
 #define ECHO_MAX_RANKS 16
 #define ECHO_MAX_ELEMENTS (INT64_C(1) << 37)
-#define ECHO_ABI_VERSION 2
+#define ECHO_ABI_VERSION 3
 
 /* ---- status codes --------------------------------------------------------- */
 #define ECHO_SUCCESS 0
@@ -276,6 +276,41 @@ int echo_call_plain(int32_t nranks, int32_t rank, int64_t n, int32_t bits, const
  * (codes1 = the echo_encode output, e2_own) on a side stream, which must finish
  * before the next call's entry pass reads the averages.  Bit-identical to
  * echo_call. */
+
+/* The same schedule with the next call's correction kept as one array, so
+ * that the critical-path entry pass reads one binary32 value per element
+ * instead of both averages ("Tensor-parallel traffic drops to 4 bits",
+ * Interpretation: the correction is fused into the entry pass and the update
+ * runs off the critical path):
+ *   echo_correction once (after echo_state_init, or whenever the averages
+ *   were changed by any other call) -> per call: echo_encode_corr ->
+ *   transport -> echo_reduce_shard -> transport -> echo_call_exit on the
+ *   critical stream; echo_update_corr on a side stream, which must finish
+ *   before the next echo_encode_corr.
+ * Bit-identical to echo_call: corr holds exactly the binary32 values
+ * (W_FAST*m_fast) + (W_SLOW*m_slow) the fused entry pass forms. */
+
+/* corr[n] = (W_FAST*m_fast) + (W_SLOW*m_slow) from the current averages
+ * ("Tensor-parallel traffic drops to 4 bits", Interpretation: the correction
+ * built from the two averages).  corr: device float[n], 16-byte aligned,
+ * caller-owned, may not overlap the averages. */
+int echo_correction(const echo_state* st, float* corr, echo_stream_t stream);
+
+/* Entry pass over all n elements from the correction array ("Tensor-parallel
+ * traffic drops to 4 bits", Interpretation): x' = f32(x) - corr, then the
+ * stage-1 quantization of echo_encode into codes / scales.  Reads x and
+ * corr only (the averages are not touched); equals echo_encode when corr
+ * came from the same averages. */
+int echo_encode_corr(const echo_state* st, const uint16_t* x, const float* corr, uint8_t* codes,
+                     float* scales, echo_stream_t stream);
+
+/* echo_update ("Tensor-parallel traffic drops to 4 bits", Interpretation:
+ * the averages absorb the residual off the critical path), then the next
+ * call's correction from the refreshed averages into corr[n].  Arguments as
+ * echo_update; corr may not overlap any of them. */
+int echo_update_corr(const echo_state* st, const uint16_t* x, const uint8_t* codes1,
+                     const float* scales1, const float* e2_own, float* corr,
+                     echo_stream_t stream);
 
 /* ---- reduce-scatter only (sequence parallelism) ------------------------------
  * The pages propose the reduce-scatter of sequence parallelism as a further

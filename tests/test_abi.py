@@ -28,7 +28,7 @@ def test_header_declares_the_calls():
                  "echo_call_exit", "echo_call_entry_range", "echo_call_plain", "echo_reduce_shard_sum",
                  "echo_rs_reduce",
                  "echo_rs_call", "echo_stream_copy", "echo_get_config", "echo_status_string",
-                 "echo_version"):
+                 "echo_version", "echo_correction", "echo_encode_corr", "echo_update_corr"):
         assert want in names
 
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_config_matches_oracle_constants():
     cfg = B.echo_get_config()
-    assert cfg["abi_version"] == B.echo_version() == 2
+    assert cfg["abi_version"] == B.echo_version() == 3
     assert cfg["qmax8"] == orc.QMAX8 == 127
     assert cfg["group"] == orc.GROUP == 128
     assert cfg["qmax"] == orc.QMAX

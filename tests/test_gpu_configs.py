@@ -193,6 +193,23 @@ class RankRun:
         B.echo_update(self.st, xd, self.send_c, self.send_s, e2, side)
         main.wait_stream(side)
 
+    def call_split_corr(self, xd, e2, corr, side):
+        """The same schedule with the correction kept as one array: the entry
+        pass reads corr, the side-stream update refreshes the averages and
+        writes the next call's corr."""
+        P, r, C, f = self.P, self.rank, self.C, self.f
+        main = torch.cuda.current_stream()
+        sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
+        sh_c = [self.send_c[r * C // f:(r + 1) * C // f] if q == r else self.recv_d[q][0] for q in range(P)]
+        sh_s = [self.send_s[r * C // 128:(r + 1) * C // 128] if q == r else self.recv_d[q][1] for q in range(P)]
+        B.echo_encode_corr(self.st, xd, corr, self.send_c, self.send_s, main)
+        B.echo_reduce_shard(sh_c, sh_s, self.own_c, self.own_s, self.y[r * C:(r + 1) * C], e2, chunk_n=C,
+                            stream=main, bits=self.bits)
+        B.echo_call_exit(self.st, sl(self.gath_d, 0), sl(self.gath_d, 1), self.y, main)
+        side.wait_stream(main)
+        B.echo_update_corr(self.st, xd, self.send_c, self.send_s, e2, corr, side)
+        main.wait_stream(side)
+
     def check_windows(self, xd, tag):
         """Run every window's oracle one call further and compare."""
         torch.cuda.synchronize()
@@ -406,12 +423,13 @@ def test_1gb_message_reduce_scatter():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("schedule", ["uncompensated", "split"])
+@pytest.mark.parametrize("schedule", ["uncompensated", "split", "split_corr"])
 def test_1gb_message_other_schedules(schedule):
-    """The bench's other 1 GB schedules: the uncompensated call, and the
-    split schedule (averages read-only on the critical path, the update on a
-    side stream); four calls, windows of every chunk after each call and
-    every output byte of the last against the oracle."""
+    """The bench's other 1 GB schedules: the uncompensated call, the split
+    schedule (averages read-only on the critical path, the update on a side
+    stream), and the split schedule with the correction kept as one array;
+    four calls, windows of every chunk after each call and every output byte
+    of the last against the oracle."""
     P, rank, n = 8, 0, 1 << 29
     say(f"1gb {schedule}: generating inputs")
     x = I.vector_with_outliers(n, I.stream_key("echo-1gb", 0, "x"), outlier_mult=20.0)
@@ -420,15 +438,24 @@ def test_1gb_message_other_schedules(schedule):
                   comp=schedule != "uncompensated", full=True)
     e2 = g.empty_f32(n // P)
     side = torch.cuda.Stream()
+    corr = None
+    if schedule == "split_corr":
+        corr = g.empty_f32(n)
+        B.echo_correction(run.st, corr)
     for call in range(4):
         if schedule == "uncompensated":
             run.call_plain(xd)
-        else:
+        elif schedule == "split":
             run.call_split(xd, e2, side)
+        else:
+            run.call_split_corr(xd, e2, corr, side)
         run.oracle_call(x)
         run.check_windows(xd, f"call {call}")
         say(f"1gb {schedule}: call {call} windows ok")
     run.full.compare("call 3")
+    if corr is not None:
+        g.eq(g.host(corr, np.float32), orc.correction(run.full.mf, run.full.ms),
+             "1gb split_corr call 3 correction array")
 
 
 @pytest.mark.parametrize("a", [1.0, 1.1])

@@ -545,6 +545,80 @@ def test_deferred_update_on_side_stream_equals_fused(P, rank, k):
                 g.eq(c1[j * Cn // 2:(j + 1) * Cn // 2], fc[j * Cn // 2:(j + 1) * Cn // 2], "send")
 
 
+@pytest.mark.parametrize("P,rank,k", [(1, 0, 3), (4, 0, 5), (8, 3, 9), (16, 11, 2)])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_deferred_update_with_correction_array(P, rank, k, bits):
+    """The deferred-update schedule with the correction kept as one array:
+    echo_encode_corr + echo_reduce_shard + echo_call_exit on the main stream,
+    echo_update_corr on a side stream; 4 calls against the oracle's fused
+    call, and the array against the oracle's correction of its averages."""
+    g = gu()
+    case = RankCase(P, rank, k, seed=67, bits=bits)
+    n, Cn, f = case.n, case.Cn, (1 if bits == 8 else 2)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    codes1, scales1 = g.empty_u8(n // f), g.empty_f32(n // 128)
+    e2 = g.empty_f32(Cn)
+    corr = g.empty_f32(n, 7.0)
+    B.echo_correction(case.st, corr, stream=main)  # from the zero averages
+    updated = None
+    for call in range(4):
+        x = x_of(n, 70 + call)
+        xd = g.dev(x)
+        if updated is not None:
+            main.wait_event(updated)  # the entry pass reads the correction the update wrote
+        B.echo_encode_corr(case.st, xd, corr, codes1, scales1, stream=main)
+        sh_c = [codes1[rank * Cn // f:(rank + 1) * Cn // f] if q == rank else case.recv_d[q][0]
+                for q in range(P)]
+        sh_s = [scales1[rank * Cn // 128:(rank + 1) * Cn // 128] if q == rank else case.recv_d[q][1]
+                for q in range(P)]
+        B.echo_reduce_shard(sh_c, sh_s, case.own_c, case.own_s, case.y[rank * Cn:(rank + 1) * Cn],
+                            e2, chunk_n=Cn, stream=main, bits=bits)
+        reduced = torch.cuda.Event()
+        reduced.record(main)
+        B.echo_call_exit(case.st, case.slot(case.gath_d, 0), case.slot(case.gath_d, 1), case.y,
+                         stream=main)
+        side.wait_event(reduced)
+        B.echo_update_corr(case.st, xd, codes1, scales1, e2, corr, stream=side)
+        updated = torch.cuda.Event()
+        updated.record(side)
+        xd.record_stream(side)
+        torch.cuda.synchronize()
+        want = case.oracle_call(x)
+        c1 = g.host(codes1, np.uint8)
+        s1 = g.host(scales1, np.float32)
+        for j in range(P):
+            if j != rank:
+                cs, gs = slice(j * Cn // f, (j + 1) * Cn // f), slice(j * Cn // 128, (j + 1) * Cn // 128)
+                eq(c1[cs], want["send_codes"][cs], f"call {call} send codes chunk {j}")
+                eq(s1[gs], want["send_scales"][gs], f"call {call} send scales chunk {j}")
+        eq(g.host(case.own_c, np.uint8), want["own_codes2"], f"call {call} own codes2")
+        eq(g.host(case.own_s, np.float32), want["own_scales2"], f"call {call} own scales2")
+        eq(g.host(case.y, np.uint16), want["y"], f"call {call} y")
+        eq(g.host(case.mfd, np.float32), case.mf, f"call {call} m_fast")
+        eq(g.host(case.msd, np.float32), case.ms, f"call {call} m_slow")
+        eq(g.host(corr, np.float32), orc.correction(case.mf, case.ms), f"call {call} correction")
+
+
+def test_correction_of_given_averages():
+    """echo_correction against the oracle's correction on averages spanning
+    large, tiny, subnormal and cancelling values."""
+    g = gu()
+    rng = np.random.default_rng(71)
+    n = 8 * 128 * 37
+    mf = (rng.standard_normal(n) * np.exp2(rng.integers(-140, 120, n))).astype(np.float32)
+    ms = (rng.standard_normal(n) * np.exp2(rng.integers(-140, 120, n))).astype(np.float32)
+    ms[::5] = -mf[::5]
+    mf[1::9] = np.finfo(np.float32).max
+    ms[1::9] = np.finfo(np.float32).max
+    mfd, msd = g.dev(mf), g.dev(ms)
+    st = B.EchoState(mfd, msd, n, 8, 2)
+    corr = g.empty_f32(n, 3.0)
+    B.echo_correction(st, corr)
+    torch.cuda.synchronize()
+    eq(g.host(corr, np.float32), orc.correction(mf, ms), "correction")
+
+
 def _adversarial_groups(rng, ngroups):
     """x' values placed on the quantizer's decision boundaries.  Each group:
     element 0 is the absmax A, s = fl(A / 7), and the rest are fl((k + 1/2) s)
