@@ -179,8 +179,39 @@ def cpu_baseline(x, recv, gath, P: int, rank: int, n_sample: int, calls: int):
     }
 
 
+def cu_partition_streams(torch, frac):
+    """Two streams over disjoint sets of compute units: `frac` of them, spread
+    evenly, for the update, the rest for the matmul.  Made before any other
+    stream: a CU-masked stream needs a hardware queue of its own."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    k = max(1, round(frac * ncu))
+    upd = sorted(set(int(i * ncu / k) for i in range(k)))
+    rest = [c for c in range(ncu) if c not in set(upd)]
+    return cu_masked_stream(torch, upd), cu_masked_stream(torch, rest), len(upd), len(rest)
+
+
+def cu_masked_stream(torch, cus):
+    """A stream whose kernels may run only on the compute units listed (HIP's
+    hipExtStreamCreateWithCUMask, default priority), wrapped for torch."""
+    import ctypes
+    import re
+
+    with open("/proc/self/maps") as f:
+        path = sorted(set(re.findall(r"(/\S*libamdhip64\.so\S*)", f.read())))[0]
+    hip = ctypes.CDLL(path)
+    words = (ctypes.c_uint32 * 32)()
+    for c in cus:
+        words[c // 32] |= 1 << (c % 32)
+    nwords = (max(cus) // 32) + 1
+    handle = ctypes.c_void_p()
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), ctypes.c_uint32(nwords), words)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({rc})")
+    return torch.cuda.ExternalStream(handle.value)
+
+
 def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, y, e2,
-              N, P, rank, steps):
+              N, P, rank, steps, cu_streams=()):
     """The compensation's cost on the critical path (in the pages' schedule
     the averages' update overlaps the following matrix multiplication).  Times, per
     call: the fused call; the uncompensated call; the split schedule's
@@ -354,6 +385,52 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
             main.wait_event(state["updated"])
             state["updated"] = None
     torch.cuda.synchronize()
+
+    # The split schedule with the compute units partitioned: the matmul on a
+    # stream limited to one part, the update on a stream limited to the other.
+    cu_rows = []
+    for s_upd, s_mm, n_upd, n_mm in cu_streams:
+
+        def b_cu(e=None, s_upd=s_upd, s_mm=s_mm):
+            wait_update()
+            if e: e[0].record(main)
+            reduced = split_corr_critical()
+            if e: e[1].record(main)
+            s_mm.wait_event(reduced)
+            with torch.cuda.stream(s_mm):
+                gemm()
+            s_upd.wait_event(reduced)
+            B.echo_update_corr(st, xd, send_c, send_s, e2, corr, s_upd)
+            ev = torch.cuda.Event()
+            ev.record(s_upd)
+            state["updated"] = ev
+            main.wait_stream(s_mm)
+
+        def b_upd_only(e=None, s_upd=s_upd):
+            s_upd.wait_stream(main)
+            if e: e[0].record(s_upd)
+            B.echo_update_corr(st, xd, send_c, send_s, e2, corr, s_upd)
+            if e: e[1].record(s_upd)
+            main.wait_stream(s_upd)
+
+        def b_mm_only(e=None, s_mm=s_mm):
+            s_mm.wait_stream(main)
+            if e: e[0].record(s_mm)
+            with torch.cuda.stream(s_mm):
+                gemm()
+            if e: e[1].record(s_mm)
+            main.wait_stream(s_mm)
+
+        wall, _ = timed(b_cu)
+        main.wait_event(state["updated"])
+        state["updated"] = None
+        _, upd_ms = timed(b_upd_only)
+        _, mm_ms = timed(b_mm_only)
+        torch.cuda.synchronize()
+        cu_rows.append({"update_cus": n_upd, "matmul_cus": n_mm,
+                        "split_corr+matmul_ms": round(wall, 4), "update_corr_alone_ms": round(upd_ms, 4),
+                        "matmul_alone_ms": round(mm_ms, 4)})
+    torch.cuda.synchronize()
     return {
         "matmul": "[%d x 4096] @ [4096 x 1792] bf16" % (N // 4096),
         "matmul_ms": round(out["gemm"][1], 4),
@@ -370,6 +447,7 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         "call_8bit_GBps": round(step_bytes(N, P, bits=8) / (out["call8"][1] * 1e-3) / 1e9, 1),
         "reduce_scatter_call_ms": round(out["rs"][1], 4),
         "reduce_scatter_GBps": round(rs_bytes(N, P) / (out["rs"][1] * 1e-3) / 1e9, 1),
+        "cu_partitioned": cu_rows,
         "compensation_on_critical_path_ms": {
             "fused": round(out["fused"][1] - out["plain"][1], 4),
             "split": round(out["split"][1] - out["plain"][1], 4),
@@ -669,6 +747,9 @@ def main() -> int:
                     help="smaller workloads: CPU time budget of the oracle leg")
     ap.add_argument("--no-schedules", action="store_true",
                     help="skip the critical-path comparison (fused / split / uncompensated)")
+    ap.add_argument("--cu-split", type=float, default=None,
+                    help="also time the split schedule with the compute units partitioned: the "
+                         "update's stream gets this fraction of the CUs and the matmul's the rest")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run a plain 1 GiB device copy (torch) before the warmup, as "
                          "the known-size reference for HBM counter runs")
@@ -700,6 +781,7 @@ def main() -> int:
     N, P, rank = 1 << args.log2n, args.nranks, 0
     C = N // P
     dev = torch.device("cuda:0")
+    cu_streams = [] if args.cu_split is None else [cu_partition_streams(torch, args.cu_split)]
     print(f"bench: generating workload N={N} P={P}", file=sys.stderr, flush=True)
     x, recv, gath = make_workload(N, P, rank)
 
@@ -813,7 +895,7 @@ def main() -> int:
         print("bench: critical-path schedules", file=sys.stderr, flush=True)
         e2 = torch.empty(C, dtype=torch.float32, device=dev)
         out["schedules"] = schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c,
-                                     own_s, y, e2, N, P, rank, args.steps)
+                                     own_s, y, e2, N, P, rank, args.steps, cu_streams)
     if not args.no_cpu:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         n_s = min(N, 1 << args.cpu_log2n)

@@ -383,10 +383,20 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
   const uint32_t nslices = (a.groups + 1u) >> 1;
 
   for (uint32_t s0 = wave * U; s0 < nslices; s0 += nwaves * U) {
+    // The arguments are read through a kernarg-segment pointer made opaque
+    // inside each step, so their loads stay in the step instead of being
+    // hoisted out of the loop and held in scalar registers across it: with
+    // 2P shard pointers live beside the rest, P >= 14 spilled scalar
+    // registers into vector lanes (P = 16: 21 spilled, occupancy 5).  A wave
+    // runs one step at full grid, so each argument is still loaded once.
+    uint64_t kp = (uint64_t)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(kp));
+    const __attribute__((address_space(4))) ReduceArgs* ar =
+        (const __attribute__((address_space(4))) ReduceArgs*)kp;
     // The own slot's index, opaque to the optimizer inside each step: left
     // loop-invariant, its P comparisons are hoisted out of the loop and held
     // as P live lane masks, which for large P spill the scalar registers.
-    int32_t own = a.rank;
+    int32_t own = ar->rank;
     asm volatile("" : "+s"(own));
     // issue every load of the U slices first
     bool ok[U];
@@ -410,18 +420,18 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
         cw[u][q] = 0u;
         sc[u][q] = 0.f;
         if (!(own_in_registers(MODE) && q == own)) {
-          cw[u][q] = load_codes4<BITS>(a.codes[q], e);
-          sc[u][q] = a.scales[q][g[u]];
+          cw[u][q] = load_codes4<BITS>(ar->codes[q], e);
+          sc[u][q] = ar->scales[q][g[u]];
         }
       }
       uint2 xw = make_uint2(0u, 0u);
       float4 f = make_float4(0.f, 0.f, 0.f, 0.f), s = make_float4(0.f, 0.f, 0.f, 0.f);
       if (own_in_registers(MODE)) {
-        const u32x2 xv = ld_stream(reinterpret_cast<const u32x2*>(a.x + e));
+        const u32x2 xv = ld_stream(reinterpret_cast<const u32x2*>(ar->x + e));
         xw = make_uint2(xv.x, xv.y);
         if (own_reads_state(MODE)) {
-          const f32x4 fv = ld_stream(reinterpret_cast<const f32x4*>(a.mf + e));
-          const f32x4 sv = ld_stream(reinterpret_cast<const f32x4*>(a.ms + e));
+          const f32x4 fv = ld_stream(reinterpret_cast<const f32x4*>(ar->mf + e));
+          const f32x4 sv = ld_stream(reinterpret_cast<const f32x4*>(ar->ms + e));
           f = make_float4(fv.x, fv.y, fv.z, fv.w);
           s = make_float4(sv.x, sv.y, sv.z, sv.w);
         }
@@ -501,12 +511,12 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
 
       if (ok[u]) {
         if (requantizes(MODE)) {
-          store_codes4<BITS>(a.out_codes, e, pack_codes4<BITS>(q2));
-          if (sub == 0) a.out_scales[g[u]] = s2;
+          store_codes4<BITS>(ar->out_codes, e, pack_codes4<BITS>(q2));
+          if (sub == 0) ar->out_scales[g[u]] = s2;
         }
-        if (a.y) st_stream(reinterpret_cast<u32x2*>(a.y + e), u32x2{y01, y23});
-        if (stores_e2(MODE) && a.e2)
-          *reinterpret_cast<float4*>(a.e2 + e) = make_float4(e2[0], e2[1], e2[2], e2[3]);
+        if (ar->y) st_stream(reinterpret_cast<u32x2*>(ar->y + e), u32x2{y01, y23});
+        if (stores_e2(MODE) && ar->e2)
+          *reinterpret_cast<float4*>(ar->e2 + e) = make_float4(e2[0], e2[1], e2[2], e2[3]);
       }
       if (own_reads_state(MODE)) {
 #pragma unroll
@@ -515,8 +525,8 @@ __global__ __launch_bounds__(kBlock) void k_reduce(ReduceArgs a) {
           refresh(mf[u][k], ms[u][k], e1 + e2[k]);
         }
         if (ok[u]) {
-          st_stream(reinterpret_cast<f32x4*>(a.mf + e), f32x4{mf[u][0], mf[u][1], mf[u][2], mf[u][3]});
-          st_stream(reinterpret_cast<f32x4*>(a.ms + e), f32x4{ms[u][0], ms[u][1], ms[u][2], ms[u][3]});
+          st_stream(reinterpret_cast<f32x4*>(ar->mf + e), f32x4{mf[u][0], mf[u][1], mf[u][2], mf[u][3]});
+          st_stream(reinterpret_cast<f32x4*>(ar->ms + e), f32x4{ms[u][0], ms[u][1], ms[u][2], ms[u][3]});
         }
       }
     }
