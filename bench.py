@@ -90,20 +90,30 @@ def traffic_from_profile(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
-def make_workload(N: int, P: int, rank: int, seed: int = 0):
+def make_messages(N: int, P: int, rank: int, seed: int = 0, which: int = 0):
+    """The seeded incoming stage-1 shards and gathered stage-2 chunks of one
+    call (set `which` of them; set 0 is the workload's own)."""
     import numpy as np
 
     from error_compensated_bit_echo_amd import inputs as I
 
     C = N // P
-    x = I.vector_with_outliers(N, I.stream_key("echo-1gb", seed, "x"), outlier_mult=20.0)
-    recv = [None if q == rank else I.int4_message(C, I.stream_key("echo-1gb", seed, "recv", q))
+    tag = ("echo-1gb", seed) if which == 0 else ("echo-1gb", seed, "set", which)
+    recv = [None if q == rank else I.int4_message(C, I.stream_key(*tag, "recv", q))
             for q in range(P)]
     # gathered stage-2 chunks carry sums of P contributions: larger scales
     gath = [None if j == rank else
-            I.int4_message(C, I.stream_key("echo-1gb", seed, "gath", j),
+            I.int4_message(C, I.stream_key(*tag, "gath", j),
                            scale_lo=0.05 * np.sqrt(P), scale_hi=0.55 * np.sqrt(P))
             for j in range(P)]
+    return recv, gath
+
+
+def make_workload(N: int, P: int, rank: int, seed: int = 0):
+    from error_compensated_bit_echo_amd import inputs as I
+
+    x = I.vector_with_outliers(N, I.stream_key("echo-1gb", seed, "x"), outlier_mult=20.0)
+    recv, gath = make_messages(N, P, rank, seed)
     return x, recv, gath
 
 
@@ -747,6 +757,8 @@ def main() -> int:
                     help="smaller workloads: CPU time budget of the oracle leg")
     ap.add_argument("--no-schedules", action="store_true",
                     help="skip the critical-path comparison (fused / split / uncompensated)")
+    ap.add_argument("--message-sets", type=int, default=1,
+                    help="distinct sets of incoming and gathered messages, cycled call by call")
     ap.add_argument("--cu-split", type=float, default=None,
                     help="also time the split schedule with the compute units partitioned: the "
                          "update's stream gets this fraction of the CUs and the matmul's the rest")
@@ -765,8 +777,8 @@ def main() -> int:
         print("bench.py measures the per-rank pipeline on one GPU; the library has no "
               "multi-GPU transport, so --gpus must be 1", file=sys.stderr)
         return 2
-    if args.steps < 1 or args.warmup < 0:
-        print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+    if args.steps < 1 or args.warmup < 0 or args.message_sets < 1:
+        print("--steps and --message-sets must be at least 1 and --warmup at least 0", file=sys.stderr)
         return 2
     if args.sweep:
         return run_sweep(args)
@@ -790,8 +802,15 @@ def main() -> int:
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
     xd = d(x)
-    rd = [None if m is None else (d(m[0]), d(m[1])) for m in recv]
-    gd = [None if m is None else (d(m[0]), d(m[1])) for m in gath]
+    # message sets cycled call by call (set 0 is the workload's own)
+    msets = [(recv, gath)] + [make_messages(N, P, rank, which=k) for k in range(1, args.message_sets)]
+    dsets = []
+    for r_h, g_h in msets:
+        rd = [None if m is None else (d(m[0]), d(m[1])) for m in r_h]
+        gd = [None if m is None else (d(m[0]), d(m[1])) for m in g_h]
+        dsets.append(([None if m is None else m[0] for m in rd], [None if m is None else m[1] for m in rd],
+                      [None if m is None else m[0] for m in gd], [None if m is None else m[1] for m in gd]))
+    del msets
     mf = torch.empty(N, dtype=torch.float32, device=dev)
     ms = torch.empty(N, dtype=torch.float32, device=dev)
     send_c = torch.empty(N // 2, dtype=torch.uint8, device=dev)
@@ -801,21 +820,21 @@ def main() -> int:
     y = torch.empty(N, dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream()
     st = B.echo_state_init(mf, ms, N, P, rank, stream)
-    rc_ = [None if m is None else m[0] for m in rd]
-    rs_ = [None if m is None else m[1] for m in rd]
-    gc_ = [None if m is None else m[0] for m in gd]
-    gs_ = [None if m is None else m[1] for m in gd]
+    rc_, rs_, gc_, gs_ = dsets[0]
+    calls = [0]
 
     def step(ev=None):
+        rc_k, rs_k, gc_k, gs_k = dsets[calls[0] % len(dsets)]
+        calls[0] += 1
         if ev is not None:
             ev[0].record(stream)
         B.echo_call_entry(st, xd, send_c, send_s, stream)
         if ev is not None:
             ev[1].record(stream)
-        B.echo_call_reduce(st, xd, rc_, rs_, own_c, own_s, y, stream)
+        B.echo_call_reduce(st, xd, rc_k, rs_k, own_c, own_s, y, stream)
         if ev is not None:
             ev[2].record(stream)
-        B.echo_call_exit(st, gc_, gs_, y, stream)
+        B.echo_call_exit(st, gc_k, gs_k, y, stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -843,8 +862,8 @@ def main() -> int:
     # the fused entry point itself, same stream, for reference
     torch.cuda.synchronize()
     t2 = time.perf_counter()
-    for _ in range(args.steps):
-        B.echo_call(st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, y, stream)
+    for k in range(args.steps):
+        B.echo_call(st, xd, *dsets[k % len(dsets)], send_c, send_s, own_c, own_s, y, stream)
     torch.cuda.synchronize()
     call_ms = (time.perf_counter() - t2) * 1e3 / args.steps
 
@@ -869,6 +888,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": workload, "elements": N, "nranks": P, "rank": rank, "group": 128,
+                   "message_sets": args.message_sets,
                    "input": "N(0,1), 0.1% of elements x20; seeded int4 shards in HBM"},
         "pct_hbm_peak": round(100.0 * total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "algorithmic_bytes_per_step": int(total_bytes),
