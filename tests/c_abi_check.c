@@ -7,8 +7,11 @@
  *                     through the phased entry points on a second state, and
  *                     through the pipelined form (entry one chunk at a time in
  *                     reverse order, reduce, exit one gathered chunk at a time
- *                     with echo_decode) on a third, each checked bit for bit
- *                     against the CPU oracle
+ *                     with echo_decode) on a third, and through the deferred-
+ *                     update schedule with the correction array
+ *                     (echo_correction, echo_encode_corr, echo_reduce_shard,
+ *                     echo_call_exit, echo_update_corr) on a fourth, each
+ *                     checked bit for bit against the CPU oracle
  *
  * Prints "ok" and exits 0 on success.  Test infrastructure: it links the
  * oracle (liborc.so) beside the library only to compare them. */
@@ -164,13 +167,14 @@ static void check_gpu(void) {
   uint16_t* o_y = (uint16_t*)malloc((size_t)n * 2);
   if (!omf || !oms || !o_send_c || !o_send_s || !o_own_c || !o_own_s || !o_y) FAIL("out of host memory");
 
-  /* device state (three: fused, phased, pipelined) and outputs */
-  float *mf[3], *ms[3];
-  echo_state st[3];
+  /* device state (four: fused, phased, pipelined, deferred update with the
+   * correction array) and outputs */
+  float *mf[4], *ms[4];
+  echo_state st[4];
   uint16_t *dx, *dy;
   uint8_t *send_c, *own_c;
-  float *send_s, *own_s;
-  for (int v = 0; v < 3; ++v) {
+  float *send_s, *own_s, *corr, *e2;
+  for (int v = 0; v < 4; ++v) {
     HIP(hipMalloc((void**)&mf[v], (size_t)n * sizeof(float)));
     HIP(hipMalloc((void**)&ms[v], (size_t)n * sizeof(float)));
     EXPECT(echo_state_init(&st[v], mf[v], ms[v], n, P, RANK, NULL) == ECHO_SUCCESS, "state init");
@@ -181,10 +185,13 @@ static void check_gpu(void) {
   HIP(hipMalloc((void**)&send_s, (size_t)(n / ECHO_GROUP) * sizeof(float)));
   HIP(hipMalloc((void**)&own_c, cb));
   HIP(hipMalloc((void**)&own_s, cs));
+  HIP(hipMalloc((void**)&corr, (size_t)n * sizeof(float)));
+  HIP(hipMalloc((void**)&e2, (size_t)C * sizeof(float)));
   hipStream_t s;
   HIP(hipStreamCreate(&s));
+  EXPECT(echo_correction(&st[3], corr, (echo_stream_t)s) == ECHO_SUCCESS, "correction");
 
-  for (int v = 0; v < 3; ++v) {
+  for (int v = 0; v < 4; ++v) {
     memset(omf, 0, (size_t)n * sizeof(float));
     memset(oms, 0, (size_t)n * sizeof(float));
     for (int c = 0; c < 3; ++c) {
@@ -199,6 +206,21 @@ static void check_gpu(void) {
                    ECHO_SUCCESS,
                "reduce");
         EXPECT(echo_call_exit(&st[1], dc[1], ds[1], dy, (echo_stream_t)s) == ECHO_SUCCESS, "exit");
+      } else if (v == 3) {
+        const uint8_t* sh_c[P];
+        const float* sh_s[P];
+        for (int q = 0; q < P; ++q) {
+          sh_c[q] = q == RANK ? send_c + RANK * cb : dc[0][q];
+          sh_s[q] = q == RANK ? send_s + RANK * (C / ECHO_GROUP) : ds[0][q];
+        }
+        EXPECT(echo_encode_corr(&st[3], dx, corr, send_c, send_s, (echo_stream_t)s) == ECHO_SUCCESS,
+               "encode from the correction");
+        EXPECT(echo_reduce_shard(P, C, 4, sh_c, sh_s, own_c, own_s, dy + RANK * C, e2, (echo_stream_t)s) ==
+                   ECHO_SUCCESS,
+               "reduce shard");
+        EXPECT(echo_call_exit(&st[3], dc[1], ds[1], dy, (echo_stream_t)s) == ECHO_SUCCESS, "exit");
+        EXPECT(echo_update_corr(&st[3], dx, send_c, send_s, e2, corr, (echo_stream_t)s) == ECHO_SUCCESS,
+               "update and correction");
       } else {
         for (int j = P - 1; j >= 0; --j)
           EXPECT(echo_call_entry_range(&st[2], dx, j, j + 1, send_c, send_s, (echo_stream_t)s) ==
@@ -218,7 +240,8 @@ static void check_gpu(void) {
                       (const uint8_t* const*)hc[1], (const float* const*)hs[1], o_send_c, o_send_s,
                       o_own_c, o_own_s, o_y, 1, 4) == 0,
              "orc_call");
-      expect_equal(dy, o_y, (size_t)n * 2, v == 0 ? "y" : v == 1 ? "phased y" : "pipelined y", c);
+      expect_equal(dy, o_y, (size_t)n * 2,
+                   v == 0 ? "y" : v == 1 ? "phased y" : v == 2 ? "pipelined y" : "deferred y", c);
       expect_equal(own_c, o_own_c, cb, "own codes2", c);
       expect_equal(own_s, o_own_s, cs, "own scales2", c);
       expect_equal(mf[v], omf, (size_t)n * sizeof(float), "m_fast", c);
@@ -232,7 +255,9 @@ static void check_gpu(void) {
   }
 
   HIP(hipStreamDestroy(s));
-  for (int v = 0; v < 3; ++v) {
+  HIP(hipFree(corr));
+  HIP(hipFree(e2));
+  for (int v = 0; v < 4; ++v) {
     HIP(hipFree(mf[v]));
     HIP(hipFree(ms[v]));
   }

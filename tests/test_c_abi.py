@@ -1,7 +1,8 @@
 """libecho from plain C11 (tests/c_abi_check.c): the header compiles as C,
 the library links without Python or torch, and -- on a GPU -- a C program
 that owns its device memory reproduces the oracle bit for bit through the
-fused and the phased entry points."""
+fused, the phased and pipelined entry points, and the deferred-update
+schedule with the correction array."""
 import os
 import shutil
 import subprocess
@@ -39,6 +40,6 @@ def test_c_consumer_without_gpu(tmp_path):
 @pytest.mark.gpu
 def test_c_consumer_on_the_gpu(tmp_path):
     exe = _build(tmp_path)
-    print("c_abi_check gpu: P=4 rank=1 n=2560, fused, phased and pipelined", flush=True)
+    print("c_abi_check gpu: P=4 rank=1 n=2560, fused, phased, pipelined and deferred", flush=True)
     r = subprocess.run([str(exe), "gpu"], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr

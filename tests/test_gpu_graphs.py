@@ -78,9 +78,10 @@ def test_captured_call_sequence_replays_bit_exact(bits):
 
 def test_captured_mixed_schedules_with_a_side_stream():
     """One captured sequence mixing the entry points: a fused call, the
-    uncompensated call, a reduce-scatter call, and the split schedule whose
-    update runs on a second stream forked and joined inside the capture.
-    Every replay equals the eager run bit for bit."""
+    uncompensated call, a reduce-scatter call, the split schedule whose
+    update runs on a second stream forked and joined inside the capture, and
+    the same schedule with the correction kept as one array.  Every replay
+    equals the eager run bit for bit."""
     P, rank, n = 8, 5, 8 * 128 * 6
     C = n // P
     xs = [g.dev(I.gaussian_outlier_channels(n // 1024, 1024, I.stream_key("mixed", l))) for l in range(4)]
@@ -94,7 +95,8 @@ def test_captured_mixed_schedules_with_a_side_stream():
     send_c, send_s = g.empty_u8(n // 2), g.empty_f32(n // 128)
     own_c, own_s = g.empty_u8(C // 2), g.empty_f32(C // 128)
     e2 = g.empty_f32(C, 0.0)
-    ys = [g.empty_bf16(n) for _ in range(3)]
+    ys = [g.empty_bf16(n) for _ in range(4)]
+    corr = g.empty_f32(n, 0.0)
     y_rs = g.empty_bf16(C)
     side = torch.cuda.Stream()
     sh_c = [send_c[rank * C // 2:(rank + 1) * C // 2] if q == rank else recv[q][0] for q in range(P)]
@@ -115,8 +117,17 @@ def test_captured_mixed_schedules_with_a_side_stream():
         side.wait_stream(main)
         B.echo_update(st, xs[3], send_c, send_s, e2, side)
         main.wait_stream(side)
+        # the same with the correction array: set up, then one call
+        B.echo_correction(st, corr, main)
+        B.echo_encode_corr(st, xs[0], corr, send_c, send_s, main)
+        B.echo_reduce_shard(sh_c, sh_s, own_c, own_s, ys[3][rank * C:(rank + 1) * C], e2, chunk_n=C,
+                            stream=main)
+        B.echo_call_exit(st, sl(gath, 0), sl(gath, 1), ys[3], main)
+        side.wait_stream(main)
+        B.echo_update_corr(st, xs[0], send_c, send_s, e2, corr, side)
+        main.wait_stream(side)
 
-    outs = lambda: [mf, ms, own_c, own_s, send_c, send_s, e2, y_rs, *ys]  # noqa: E731
+    outs = lambda: [mf, ms, own_c, own_s, send_c, send_s, e2, y_rs, corr, *ys]  # noqa: E731
     sequence()
     torch.cuda.synchronize()
     want = [t.clone() for t in outs()]
