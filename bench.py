@@ -192,13 +192,18 @@ def cpu_baseline(x, recv, gath, P: int, rank: int, n_sample: int, calls: int):
 
 
 def cu_partition_streams(torch, frac):
-    """Two streams over disjoint sets of compute units: `frac` of them, spread
-    evenly, for the update, the rest for the matmul.  Made before any other
-    stream: a CU-masked stream needs a hardware queue of its own."""
+    """Two streams over disjoint sets of compute units, made before any other
+    stream (a CU-masked stream needs a hardware queue of its own): in every
+    32-CU word of the mask, the low `frac` of the CUs for the update and the
+    rest for the matmul.  The runtime on MI355X accepts masks whose set bits
+    come in whole runs of 8 within each word (measured: 0xFF, 0xFFFF,
+    0x00FF00FF, 0xFFFFFF00 per word work; 0x0F, 0x0F0F0F0F, 0x33333333,
+    0x55555555 are refused with hipErrorOutOfMemory), so frac is rounded to a
+    multiple of 1/4."""
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
-    k = max(1, round(frac * ncu))
-    upd = sorted(set(int(i * ncu / k) for i in range(k)))
-    rest = [c for c in range(ncu) if c not in set(upd)]
+    k = min(24, max(8, 8 * round(frac * 4)))  # CUs of each 32 for the update
+    upd = [c for c in range(ncu) if c % 32 < k]
+    rest = [c for c in range(ncu) if c % 32 >= k]
     return cu_masked_stream(torch, upd), cu_masked_stream(torch, rest), len(upd), len(rest)
 
 
