@@ -326,3 +326,21 @@ def test_prepared_call_refuses_a_changed_state():
         call(stream=0)
     # the copy the library would read keeps the prepared width
     assert call._snap.bits == 4
+
+
+def test_library_reports_only_its_own_launch_status():
+    """The library launches through hipLaunchKernel, whose return value is that
+    launch's status, and never reads the thread's last-error slot
+    (hipGetLastError / hipPeekAtLastError are not even imported), so an error
+    an earlier, unrelated HIP call left behind can neither be reported as an
+    echo_* call's ECHO_ERR_HIP nor be cleared by it."""
+    import shutil
+    import subprocess
+
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    assert "hipLaunchKernel" in imported
+    assert not imported & {"hipGetLastError", "hipPeekAtLastError", "hipExtGetLastError"}
