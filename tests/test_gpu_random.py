@@ -1,7 +1,8 @@
 """Seeded random sweep of the GPU path against the oracle: drawn rank counts,
 ranks, chunk lengths (1 to 40 groups: every parity of the last wave's slice),
 code widths, input magnitudes and entry points (fused call, in place, the
-phased calls, the uncompensated call, the reduce-scatter call), two calls
+phased calls, the uncompensated call, the reduce-scatter call, the
+deferred-update schedule with and without the correction array), two calls
 each with the averages carried.  Bit-exact."""
 import numpy as np
 import pytest
@@ -14,7 +15,7 @@ from test_gpu_parity import RankCase, eq
 
 pytestmark = pytest.mark.gpu
 
-MODES = ("call", "in_place", "phased", "plain", "rs")
+MODES = ("call", "in_place", "phased", "plain", "rs", "split", "split_corr")
 
 
 def _cases(count=300, seed=2026):
@@ -41,6 +42,13 @@ def test_random_sweep_bit_exact():
         print(f"random sweep: case {case}", flush=True)
         rc = RankCase(P, rank, k, seed=5000 + case["i"], bits=bits)
         what = f"case {case['i']} ({mode}, P={P}, rank={rank}, k={k}, bits={bits})"
+        f = 1 if bits == 8 else 2
+        if mode.startswith("split"):
+            codes1, scales1 = g.empty_u8(rc.n // f), g.empty_f32(rc.n // 128)
+            e2 = g.empty_f32(rc.Cn)
+            corr = g.empty_f32(rc.n, 5.0)
+            if mode == "split_corr":
+                B.echo_correction(rc.st, corr)
         for call in range(2):
             x = _x(rc.n, case, call)
             xd = g.dev(x)
@@ -58,6 +66,36 @@ def test_random_sweep_bit_exact():
                     B.echo_call_exit(rc.st, rc.slot(rc.gath_d, 0), rc.slot(rc.gath_d, 1), rc.y)
                     y = rc.y
                 rc.check(rc.oracle_call(x), y=y)
+            elif mode.startswith("split"):
+                Cn = rc.Cn
+                if mode == "split":
+                    B.echo_encode(rc.st, xd, codes1, scales1)
+                else:
+                    B.echo_encode_corr(rc.st, xd, corr, codes1, scales1)
+                sh_c = [codes1[rank * Cn // f:(rank + 1) * Cn // f] if q == rank else rc.recv_d[q][0]
+                        for q in range(P)]
+                sh_s = [scales1[rank * Cn // 128:(rank + 1) * Cn // 128] if q == rank else rc.recv_d[q][1]
+                        for q in range(P)]
+                B.echo_reduce_shard(sh_c, sh_s, rc.own_c, rc.own_s, rc.y[rank * Cn:(rank + 1) * Cn], e2,
+                                    chunk_n=Cn, bits=bits)
+                B.echo_call_exit(rc.st, rc.slot(rc.gath_d, 0), rc.slot(rc.gath_d, 1), rc.y)
+                if mode == "split":
+                    B.echo_update(rc.st, xd, codes1, scales1, e2)
+                else:
+                    B.echo_update_corr(rc.st, xd, codes1, scales1, e2, corr)
+                want = rc.oracle_call(x)
+                eq(g.host(rc.y, np.uint16), want["y"], what + " y")
+                eq(g.host(rc.own_c, np.uint8), want["own_codes2"], what + " own codes2")
+                eq(g.host(rc.own_s, np.float32), want["own_scales2"], what + " own scales2")
+                eq(g.host(rc.mfd, np.float32), rc.mf, what + " m_fast")
+                eq(g.host(rc.msd, np.float32), rc.ms, what + " m_slow")
+                c1 = g.host(codes1, np.uint8)
+                for j in range(P):
+                    if j != rank:
+                        cs = slice(j * Cn // f, (j + 1) * Cn // f)
+                        eq(c1[cs], want["send_codes"][cs], what + f" send chunk {j}")
+                if mode == "split_corr":
+                    eq(g.host(corr, np.float32), orc.correction(rc.mf, rc.ms), what + " correction")
             elif mode == "plain":
                 B.echo_call_plain(P, rank, xd, rc.slot(rc.recv_d, 0), rc.slot(rc.recv_d, 1),
                                   rc.slot(rc.gath_d, 0), rc.slot(rc.gath_d, 1), rc.send_c, rc.send_s,
