@@ -344,3 +344,20 @@ def test_library_reports_only_its_own_launch_status():
     imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
     assert "hipLaunchKernel" in imported
     assert not imported & {"hipGetLastError", "hipPeekAtLastError", "hipExtGetLastError"}
+
+
+def test_correction_array_rejections():
+    """echo_correction / echo_encode_corr / echo_update_corr check their
+    arguments before launching (every call below is rejected)."""
+    s = st()  # n = 1024, P = 2: averages at A and 2A
+    assert rc(B.echo_correction, s, None) == -1
+    assert rc(B.echo_correction, s, 3 * A + 4) == -3
+    assert rc(B.echo_correction, s, A + 512) == -6          # corr over m_fast
+    assert rc(B.echo_encode_corr, s, 3 * A, None, 4 * A, 5 * A) == -1
+    assert rc(B.echo_encode_corr, s, 3 * A, 6 * A + 8, 4 * A, 5 * A) == -3
+    assert rc(B.echo_encode_corr, s, 3 * A, 6 * A, 6 * A + 64, 5 * A) == -6  # codes over corr
+    assert rc(B.echo_encode_corr, st(n=1000), 3 * A, 6 * A, 4 * A, 5 * A) == -2
+    assert rc(B.echo_update_corr, s, 3 * A, 4 * A, 5 * A, 6 * A, None) == -1
+    assert rc(B.echo_update_corr, s, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A + 4) == -3
+    assert rc(B.echo_update_corr, s, 3 * A, 4 * A, 5 * A, 6 * A, 2 * A + 256) == -6  # corr over m_slow
+    assert rc(B.echo_update_corr, s, 3 * A, 4 * A, 5 * A, 6 * A, 3 * A) == -6        # corr over x
