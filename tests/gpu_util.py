@@ -65,41 +65,46 @@ class GpuRank:
         self.mf = dev(mf.astype(np.float32))
         self.ms = dev(ms.astype(np.float32))
         self.st = B.EchoState(self.mf, self.ms, n, nranks, rank)
-        self.codes1 = empty_u8(n // 2)
+        # room for either code width (one byte per element at 8 bits)
+        self.codes1 = empty_u8(n)
         self.scales1 = empty_f32(n // 128)
-        self.send_codes = empty_u8(n // 2)
+        self.send_codes = empty_u8(n)
         self.send_scales = empty_f32(n // 128)
         self.y = empty_bf16(n)
 
 
-def gpu_simulate_call(ranks, xs_np):
+def gpu_simulate_call(ranks, xs_np, bits=4):
     """One call of P logical ranks on the GPU: every rank's entry pass
     (echo_encode, state read-only), the reduce of every chunk from the
     ranks' stage-1 chunks (echo_reduce_shard), then each rank's fused
     echo_call fed with those chunks, which re-derives its own chunk, writes
-    y and refreshes its state.  Returns (codes2, scales2, y per rank)."""
+    y and refreshes its state.  `bits` is the call's code width.  Returns
+    (codes2, scales2, own codes2 per rank, own scales2 per rank)."""
     P = len(ranks)
     n = ranks[0].n
     Cn = n // P
+    f = 1 if bits == 8 else 2  # elements per code byte
+    cb = Cn // f
     for r, x in zip(ranks, xs_np):
+        r.st.bits = bits
         r.x.copy_(dev(x))
-        B.echo_encode(r.st, r.x, r.codes1, r.scales1)
-    codes2 = empty_u8(n // 2)
+        B.echo_encode(r.st, r.x, r.codes1[:n // f], r.scales1)
+    codes2 = empty_u8(n // f)
     scales2 = empty_f32(n // 128)
     for j in range(P):
-        B.echo_reduce_shard([r.codes1[j * Cn // 2:(j + 1) * Cn // 2] for r in ranks],
+        B.echo_reduce_shard([r.codes1[j * cb:(j + 1) * cb] for r in ranks],
                             [r.scales1[j * Cn // 128:(j + 1) * Cn // 128] for r in ranks],
-                            codes2[j * Cn // 2:(j + 1) * Cn // 2],
-                            scales2[j * Cn // 128:(j + 1) * Cn // 128], chunk_n=Cn)
-    own2 = [empty_u8(Cn // 2) for _ in range(P)]
+                            codes2[j * cb:(j + 1) * cb],
+                            scales2[j * Cn // 128:(j + 1) * Cn // 128], chunk_n=Cn, bits=bits)
+    own2 = [empty_u8(cb) for _ in range(P)]
     own2s = [empty_f32(Cn // 128) for _ in range(P)]
     for p, r in enumerate(ranks):
-        recv_c = [None if q == p else ranks[q].codes1[p * Cn // 2:(p + 1) * Cn // 2] for q in range(P)]
+        recv_c = [None if q == p else ranks[q].codes1[p * cb:(p + 1) * cb] for q in range(P)]
         recv_s = [None if q == p else ranks[q].scales1[p * Cn // 128:(p + 1) * Cn // 128]
                   for q in range(P)]
-        gath_c = [None if j == p else codes2[j * Cn // 2:(j + 1) * Cn // 2] for j in range(P)]
+        gath_c = [None if j == p else codes2[j * cb:(j + 1) * cb] for j in range(P)]
         gath_s = [None if j == p else scales2[j * Cn // 128:(j + 1) * Cn // 128] for j in range(P)]
-        B.echo_call(r.st, r.x, recv_c, recv_s, gath_c, gath_s, r.send_codes, r.send_scales,
+        B.echo_call(r.st, r.x, recv_c, recv_s, gath_c, gath_s, r.send_codes[:n // f], r.send_scales,
                     own2[p], own2s[p], r.y)
     torch.cuda.synchronize()
     return codes2, scales2, own2, own2s

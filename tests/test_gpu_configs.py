@@ -5,7 +5,8 @@ the launch configuration bench.py times.
            from zero state: every output of every rank against the oracle's
            full simulation.
   decode   P=8 simulated, [256 x 4096] per rank, 64 calls with the averages
-           carried: every output, every call.
+           carried: every output, every call; also under the serving policy
+           (first half of the layers with 8-bit codes).
   prefill  rank mode, [8192 x 4096] (32M elements), 4 warm-up calls then the
            measured call; sampled windows of every chunk checked after every
            call (the oracle follows each window through the whole sequence),
@@ -43,14 +44,15 @@ def say(*a):
 
 # ---- full simulation ------------------------------------------------------------------
 
-def _simulate_sequence(P, n, calls, make_x, label):
+def _simulate_sequence(P, n, calls, make_x, label, bits_of=lambda call: 4):
     mf = [np.zeros(n, np.float32) for _ in range(P)]
     ms = [np.zeros(n, np.float32) for _ in range(P)]
     ranks = [g.GpuRank(np.zeros(n, np.uint16), mf[p], ms[p], P, p) for p in range(P)]
     for call in range(calls):
         xs = [make_x(call, p) for p in range(P)]
-        codes2, scales2, _, _ = g.gpu_simulate_call(ranks, xs)
-        want = orc.simulate(xs, mf, ms)
+        bits = bits_of(call)
+        codes2, scales2, _, _ = g.gpu_simulate_call(ranks, xs, bits=bits)
+        want = orc.simulate(xs, mf, ms, bits=bits)
         g.eq(g.host(codes2, np.uint8), want["codes2"], f"{label} call {call} codes2")
         g.eq(g.host(scales2, np.float32), want["scales2"], f"{label} call {call} scales2")
         for p, r in enumerate(ranks):
@@ -79,6 +81,21 @@ def test_config_decode_full_simulation():
     def make_x(call, p):
         return I.lognormal_channel_activations(tokens, hidden, I.stream_key("decode", 0, call, p), ck)
     _simulate_sequence(P, tokens * hidden, 64, make_x, "decode")
+
+
+@pytest.mark.timeout(600)
+def test_config_decode_serving_policy():
+    """The decode workload under the pages' serving policy: the first half of
+    the layers (calls 0-31) with 8-bit codes, the rest with 4-bit codes, one
+    state carried through all 64 calls; every output of every rank, every
+    call, against the oracle's full simulation."""
+    P, tokens, hidden = 8, 256, 4096
+    ck = I.stream_key("decode", 1, "channels")
+
+    def make_x(call, p):
+        return I.lognormal_channel_activations(tokens, hidden, I.stream_key("decode", 1, call, p), ck)
+    _simulate_sequence(P, tokens * hidden, 64, make_x, "decode 8/4-bit",
+                       bits_of=lambda call: 8 if call < 32 else 4)
 
 
 # ---- rank mode --------------------------------------------------------------------------

@@ -404,7 +404,8 @@ def test_deterministic():
 
 
 @pytest.mark.parametrize("P,k,calls", [(2, 1, 3), (3, 2, 3), (8, 4, 4)])
-def test_full_simulation_small(P, k, calls):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_full_simulation_small(P, k, calls, bits):
     """P logical ranks on one GPU (each rank's encode, every chunk's reduce,
     each rank's fused call) against the oracle's full simulation."""
     g = gu()
@@ -415,8 +416,8 @@ def test_full_simulation_small(P, k, calls):
     ranks = [g.GpuRank(np.zeros(n, np.uint16), mf[p], ms[p], P, p) for p in range(P)]
     for call in range(calls):
         xs = [x_of(n, 1000 * call + p) for p in range(P)]
-        codes2, scales2, own2, own2s = g.gpu_simulate_call(ranks, xs)
-        want = orc.simulate(xs, mf, ms)
+        codes2, scales2, own2, own2s = g.gpu_simulate_call(ranks, xs, bits=bits)
+        want = orc.simulate(xs, mf, ms, bits=bits)
         eq(g.host(codes2, np.uint8), want["codes2"], "codes2")
         eq(g.host(scales2, np.float32), want["scales2"], "scales2")
         for p, r in enumerate(ranks):
