@@ -626,28 +626,41 @@ def run_workload(args) -> int:
         xs = [I.device_lognormal_channel_activations(n // 1024, 1024, 1000 + c, lam, dev)
               for c in range(calls // 2)]
         xs += [I.device_student_t3(n, 2000 + c, dev) for c in range(calls // 2)]
-    recv_h = [None if q == rank else I.int4_message(C, I.stream_key("w-recv", q)) for q in range(P)]
-    gath_h = [None if j == rank else I.int4_message(C, I.stream_key("w-gath", j), scale_lo=0.15, scale_hi=1.5)
-              for j in range(P)]
-    recv = [None if m is None else tuple(d(t) for t in m) for m in recv_h]
-    gath = [None if m is None else tuple(d(t) for t in m) for m in gath_h]
-    rc_ = [None if m is None else m[0] for m in recv]
-    rs_ = [None if m is None else m[1] for m in recv]
-    gc_ = [None if m is None else m[0] for m in gath]
-    gs_ = [None if m is None else m[1] for m in gath]
+    # the serving policy of the pages: the first half of the layers' calls
+    # carry 8-bit codes, the rest 4-bit codes
+    bits_of = [8 if args.serving_policy and c < calls // 2 else 4 for c in range(calls)]
+    msgs_h = {}
+    for bits in sorted(set(bits_of)):
+        recv_h = [None if q == rank else I.int4_message(C, I.stream_key("w-recv", q), bits=bits)
+                  for q in range(P)]
+        gath_h = [None if j == rank else I.int4_message(C, I.stream_key("w-gath", j), scale_lo=0.15,
+                                                        scale_hi=1.5, bits=bits) for j in range(P)]
+        msgs_h[bits] = (recv_h, gath_h)
+    msgs_d = {}
+    for bits, (recv_h, gath_h) in msgs_h.items():
+        recv = [None if m is None else tuple(d(t) for t in m) for m in recv_h]
+        gath = [None if m is None else tuple(d(t) for t in m) for m in gath_h]
+        msgs_d[bits] = ([None if m is None else m[0] for m in recv], [None if m is None else m[1] for m in recv],
+                        [None if m is None else m[0] for m in gath], [None if m is None else m[1] for m in gath])
     nstates = 2 if args.workload == "train" else 1
     mem = [(torch.empty(n, device=dev), torch.empty(n, device=dev)) for _ in range(nstates)]
     stream = torch.cuda.current_stream()
     states = [B.echo_state_init(a, b, n, P, rank, stream) for a, b in mem]
-    send_c = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    # the same averages seen by 8-bit calls
+    states8 = [B.EchoState(a, b, n, P, rank, bits=8) for a, b in mem]
+    send_c = torch.empty(n, dtype=torch.uint8, device=dev)  # room for 8-bit codes
     send_s = torch.empty(n // 128, dtype=torch.float32, device=dev)
-    own_c = torch.empty(C // 2, dtype=torch.uint8, device=dev)
+    own_c = torch.empty(C, dtype=torch.uint8, device=dev)
     own_s = torch.empty(C // 128, dtype=torch.float32, device=dev)
     ys = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(calls)]
 
     # one prepared call per call of the step (arguments marshalled once)
-    prepared = [B.echo_call_prepare(states[0] if c < calls // nstates or nstates == 1 else states[1],
-                                    xs[c], rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s, ys[c])
+    def state_of(c):
+        k = 0 if c < calls // nstates or nstates == 1 else 1
+        return states8[k] if bits_of[c] == 8 else states[k]
+
+    prepared = [B.echo_call_prepare(state_of(c), xs[c], *msgs_d[bits_of[c]], send_c, send_s, own_c, own_s,
+                                    ys[c])
                 for c in range(calls)]
 
     def step():
@@ -685,16 +698,17 @@ def run_workload(args) -> int:
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     best = min(eager_ms, graph_ms) if graph_ms else eager_ms
-    per_call = step_bytes(n, P)
+    per_call = sum(step_bytes(n, P, bits=b) for b in bits_of) / calls
+    policy = " (serving policy: first half of the calls 8-bit)" if args.serving_policy else ""
     out = {
-        "metric": f"GB/s of bf16 payload through fused Echo rank pipeline @{args.workload} workload; "
+        "metric": f"GB/s of bf16 payload through fused Echo rank pipeline @{args.workload} workload{policy}; "
                   "% HBM peak",
         "value": round(2.0 * n * calls / (best * 1e-3) / 1e9, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(best, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {desc}", "elements": n, "nranks": P, "rank": rank,
-                   "calls_per_step": calls},
+        "config": {"workload": f"{args.workload}: {desc}{policy}", "elements": n, "nranks": P, "rank": rank,
+                   "calls_per_step": calls, "calls_8bit": bits_of.count(8)},
         "us_per_call": round(best * 1e3 / calls, 2),
         "eager_ms_per_step": round(eager_ms, 4),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
@@ -702,12 +716,12 @@ def run_workload(args) -> int:
         "algorithmic_bytes_per_call": int(per_call),
     }
     out["cpu_baseline"] = None if args.no_cpu else workload_cpu_baseline(
-        xs, recv_h, gath_h, P, rank, nstates, args.cpu_seconds)
+        xs, msgs_h, bits_of, P, rank, nstates, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
 
-def workload_cpu_baseline(xs, recv_h, gath_h, P: int, rank: int, nstates: int, budget_s: float):
+def workload_cpu_baseline(xs, msgs_h, bits_of, P: int, rank: int, nstates: int, budget_s: float):
     """The CPU oracle as it stands on the workload's own call sequence, from
     zero state (one state per direction for the training step): the first
     call on one thread, then the step's calls in order on all host cores
@@ -721,19 +735,20 @@ def workload_cpu_baseline(xs, recv_h, gath_h, P: int, rank: int, nstates: int, b
     calls = len(xs)
     T = oracle_threads()
     sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
-    rc, rs, gc, gs = sl(recv_h, 0), sl(recv_h, 1), sl(gath_h, 0), sl(gath_h, 1)
+    msgs = {b: (sl(r, 0), sl(r, 1), sl(g, 0), sl(g, 1)) for b, (r, g) in msgs_h.items()}
     x0 = xs[0].cpu().numpy().view(np.uint16)
     mf, ms = np.zeros(n, np.float32), np.zeros(n, np.float32)
     t0 = time.perf_counter()
-    orc.call(P, rank, x0, mf, ms, rc, rs, gc, gs, threads=1)
+    orc.call(P, rank, x0, mf, ms, *msgs[bits_of[0]], threads=1, bits=bits_of[0])
     dt1 = time.perf_counter() - t0
     states = [(np.zeros(n, np.float32), np.zeros(n, np.float32)) for _ in range(nstates)]
-    done, spent, out = 0, 0.0, None
+    done, spent, outs = 0, 0.0, {}
     while done < calls and (done == 0 or spent < budget_s):
         x = xs[done].cpu().numpy().view(np.uint16)
         mf, ms = states[0] if nstates == 1 or done < calls // nstates else states[1]
+        b = bits_of[done]
         t0 = time.perf_counter()
-        out = orc.call(P, rank, x, mf, ms, rc, rs, gc, gs, threads=T, out=out)
+        outs[b] = orc.call(P, rank, x, mf, ms, *msgs[b], threads=T, out=outs.get(b), bits=b)
         spent += time.perf_counter() - t0
         done += 1
     return {
@@ -778,6 +793,9 @@ def main() -> int:
                     help="instead of the headline: time per fused call for 2^16 .. 2^29 elements")
     ap.add_argument("--graph", action="store_true",
                     help="smaller workloads: also time the step captured in a HIP graph")
+    ap.add_argument("--serving-policy", action="store_true",
+                    help="tiny/decode workloads: the first half of the calls (layers) with 8-bit codes, "
+                         "as the pages serve Llama-3-8B")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -786,6 +804,9 @@ def main() -> int:
         return 2
     if args.steps < 1 or args.warmup < 0 or args.message_sets < 1:
         print("--steps and --message-sets must be at least 1 and --warmup at least 0", file=sys.stderr)
+        return 2
+    if args.serving_policy and args.workload not in ("tiny", "decode"):
+        print("--serving-policy applies to the serving workloads (tiny, decode)", file=sys.stderr)
         return 2
     if args.sweep:
         return run_sweep(args)

@@ -56,3 +56,12 @@ def test_step_counts_are_checked():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "0"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "--steps" in r.stderr
+
+
+def test_serving_policy_only_for_serving_workloads():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "train",
+                        "--serving-policy"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "serving" in r.stderr
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--message-sets", "0"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "--message-sets" in r.stderr
