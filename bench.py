@@ -880,11 +880,9 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    k_ms = {
-        "entry": float(np.mean([e[0].elapsed_time(e[1]) for e in events])),
-        "reduce": float(np.mean([e[1].elapsed_time(e[2]) for e in events])),
-        "exit": float(np.mean([e[2].elapsed_time(e[3]) for e in events])),
-    }
+    k_each = {name: [e[i].elapsed_time(e[i + 1]) for e in events]
+              for i, name in enumerate(("entry", "reduce", "exit"))}
+    k_ms = {name: float(np.mean(v)) for name, v in k_each.items()}
     call_event_ms = [e[0].elapsed_time(e[3]) for e in events]
 
     # the fused entry point itself, same stream, for reference
@@ -921,6 +919,8 @@ def main() -> int:
         "pct_hbm_peak": round(100.0 * total_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "algorithmic_bytes_per_step": int(total_bytes),
         "kernel_ms": {k: round(v, 4) for k, v in k_ms.items()},
+        "kernel_ms_min_max": {k: [round(float(min(v)), 4), round(float(max(v)), 4)]
+                              for k, v in k_each.items()},
         "call_ms_events": {"mean": round(float(np.mean(call_event_ms)), 4),
                            "median": round(float(np.median(call_event_ms)), 4)},
         "echo_call_ms": round(call_ms, 4),
