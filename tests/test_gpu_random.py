@@ -1,4 +1,4 @@
-"""Seeded random sweep of the GPU path against the oracle: drawn rank counts,
+"""Seeded random sweep (1500 cases) of the GPU path against the oracle: drawn rank counts,
 ranks, chunk lengths (1 to 40 groups: every parity of the last wave's slice),
 code widths, input magnitudes and entry points (fused call, in place, the
 phased calls, the uncompensated call, the reduce-scatter call, the
@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 MODES = ("call", "in_place", "phased", "plain", "rs", "split", "split_corr")
 
 
-def _cases(count=300, seed=2026):
+def _cases(count=1500, seed=2026):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(count):
