@@ -111,6 +111,27 @@ def test_decode(k, bits):
     eq(g.host(y, np.uint16), orc.decode(c, s, n, bits=bits), "y")
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_decode_bf16_narrowing_every_upper_half(bits):
+    """The exit pass's binary32 -> bf16 narrowing on every finite upper half
+    (sign, exponent, 7 kept mantissa bits), each with exact, tie, near-tie and
+    other lower halves: with every code 1 each group's products are its scale
+    itself, so y = bf16(scale) (ties to even, overflow to inf, denormals)."""
+    g = gu()
+    hi = np.arange(1 << 16, dtype=np.uint32)
+    hi = hi[(hi & 0x7F80) != 0x7F80]
+    lows = np.array([0x0000, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x1234, 0xC000], np.uint32)
+    s = ((hi[:, None] << 16) | lows[None, :]).ravel().view(np.float32)
+    n = 128 * s.size
+    c = np.full(n if bits == 8 else n // 2, 0x01 if bits == 8 else 0x11, np.uint8)
+    y = g.empty_bf16(n)
+    B.echo_decode(g.dev(c), g.dev(s), y, bits=bits)
+    want = orc.decode(c, s, n, bits=bits)
+    got = g.host(y, np.uint16)
+    eq(got, want, "y")
+    eq(got[::128], orc.f32_to_bf16(s), "y of each group vs bf16(scale)")
+
+
 def _loaded_hip_runtime():
     """The HIP runtime this process already loaded (torch's, which libecho
     shares), opened by its path so both handles are the same library."""
