@@ -354,10 +354,21 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         if e: e[1].record(main)
 
     y_own = torch.empty(C, dtype=torch.int16, device=y.device)
+    # The reduce-scatter call has no exit pass, whose loads would push the
+    # incoming shards out of the 256 MB Infinity Cache between calls, and its
+    # entry pass is non-temporal: calls on one message set would find the
+    # previous call's shards (238 MB) cached.  Three copies, cycled, keep
+    # every call's shards coming from HBM, as a fresh message's would.
+    NSETS = 3
+    rs_sets = [(rc_, rs_)] + [([None if t is None else t.clone() for t in rc_],
+                               [None if t is None else t.clone() for t in rs_]) for _ in range(NSETS - 1)]
+    turn = {"rs": 0, "call8": 0}
 
     def b_rs(e=None):
+        rc_k, rs_k = rs_sets[turn["rs"] % NSETS]
+        turn["rs"] += 1
         if e: e[0].record(main)
-        B.echo_rs_call(st, xd, rc_, rs_, send_c, send_s, y_own, main)
+        B.echo_rs_call(st, xd, rc_k, rs_k, send_c, send_s, y_own, main)
         if e: e[1].record(main)
 
     # the 8-bit promotion of a call: the same call with one byte per code
@@ -372,16 +383,23 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
         sc = torch.rand(C // 128, device=y.device, generator=g8) * 0.01 + 0.001
         return c, sc
 
-    m8 = [None if q == rank else msg8() for q in range(P)]
-    rc8 = [None if m is None else m[0] for m in m8]
-    rs8 = [None if m is None else m[1] for m in m8]
+    def set8():
+        # incoming shards and gathered chunks of one 8-bit call, distinct buffers
+        m8 = [None if q == rank else msg8() for q in range(P)]
+        g8m = [None if q == rank else msg8() for q in range(P)]
+        return ([None if m is None else m[0] for m in m8], [None if m is None else m[1] for m in m8],
+                [None if m is None else m[0] for m in g8m], [None if m is None else m[1] for m in g8m])
+
+    sets8 = [set8() for _ in range(NSETS)]
     send_c8 = torch.empty(N, dtype=torch.uint8, device=y.device)
     own_c8 = torch.empty(C, dtype=torch.uint8, device=y.device)
 
     def b_call8(e=None):
+        rc8, rs8, gc8, gs8 = sets8[turn["call8"] % NSETS]
+        turn["call8"] += 1
         st.bits = 8
         if e: e[0].record(main)
-        B.echo_call(st, xd, rc8, rs8, rc8, rs8, send_c8, send_s, own_c8, own_s, y, main)
+        B.echo_call(st, xd, rc8, rs8, gc8, gs8, send_c8, send_s, own_c8, own_s, y, main)
         if e: e[1].record(main)
         st.bits = 4
 
