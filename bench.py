@@ -19,6 +19,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -490,6 +491,9 @@ def schedules(B, torch, st, xd, rc_, rs_, gc_, gs_, send_c, send_s, own_c, own_s
     }
 
 
+# message sets cycled by the smaller workloads (see run_workload)
+MESSAGE_POOL = 16
+
 WORKLOADS = {
     # name: (elements per rank, calls per step, description)
     "tiny": (16 * 4096, 4, "bf16 [16 x 4096] per rank, N(0,1), 0.1% of channels x20; 4 calls per step"),
@@ -611,8 +615,10 @@ def calibration_copy(dev) -> None:
 
 def run_workload(args) -> int:
     """Per-rank timing of the smaller workloads (rank 0 of P = 8): a step is
-    the workload's whole call sequence; inputs differ call to call.  With
-    --graph the step is also captured once in a HIP graph and replayed."""
+    the workload's whole call sequence; inputs differ call to call, and the
+    messages come from a pool of sets cycled call by call.  With --graph each
+    of the pool's step variants is also captured in a HIP graph and the
+    graphs are replayed in turn."""
     import numpy as np
     import torch
 
@@ -647,19 +653,26 @@ def run_workload(args) -> int:
     # the serving policy of the pages: the first half of the layers' calls
     # carry 8-bit codes, the rest 4-bit codes
     bits_of = [8 if args.serving_policy and c < calls // 2 else 4 for c in range(calls)]
-    msgs_h = {}
-    for bits in sorted(set(bits_of)):
-        recv_h = [None if q == rank else I.int4_message(C, I.stream_key("w-recv", q), bits=bits)
-                  for q in range(P)]
-        gath_h = [None if j == rank else I.int4_message(C, I.stream_key("w-gath", j), scale_lo=0.15,
-                                                        scale_hi=1.5, bits=bits) for j in range(P)]
-        msgs_h[bits] = (recv_h, gath_h)
+    # Incoming shards and gathered chunks: K seeded sets drawn on the device;
+    # call g of the run (counted over steps) takes set g % K.  A set is read
+    # again only after K - 1 others, and at the prefill and training sizes the
+    # K sets hold about twice the 256 MB Infinity Cache, so their calls read
+    # every message from HBM as fresh messages would be (one set re-read call
+    # after call would stay cached: 5% faster there).  At the decode and tiny
+    # sizes all K sets fit the cache, as the messages of a whole step do.
+    K = MESSAGE_POOL
+    sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
     msgs_d = {}
-    for bits, (recv_h, gath_h) in msgs_h.items():
-        recv = [None if m is None else tuple(d(t) for t in m) for m in recv_h]
-        gath = [None if m is None else tuple(d(t) for t in m) for m in gath_h]
-        msgs_d[bits] = ([None if m is None else m[0] for m in recv], [None if m is None else m[1] for m in recv],
-                        [None if m is None else m[0] for m in gath], [None if m is None else m[1] for m in gath])
+    for bits in sorted(set(bits_of)):
+        pool = []
+        for k in range(K):
+            recv = [None if q == rank else I.device_message(C, I.stream_key("w-recv", k, q, bits), dev, bits=bits)
+                    for q in range(P)]
+            gath = [None if j == rank else I.device_message(C, I.stream_key("w-gath", k, j, bits), dev,
+                                                            scale_lo=0.15, scale_hi=1.5, bits=bits)
+                    for j in range(P)]
+            pool.append((sl(recv, 0), sl(recv, 1), sl(gath, 0), sl(gath, 1)))
+        msgs_d[bits] = pool
     nstates = 2 if args.workload == "train" else 1
     mem = [(torch.empty(n, device=dev), torch.empty(n, device=dev)) for _ in range(nstates)]
     stream = torch.cuda.current_stream()
@@ -677,42 +690,48 @@ def run_workload(args) -> int:
         k = 0 if c < calls // nstates or nstates == 1 else 1
         return states8[k] if bits_of[c] == 8 else states[k]
 
-    prepared = [B.echo_call_prepare(state_of(c), xs[c], *msgs_d[bits_of[c]], send_c, send_s, own_c, own_s,
-                                    ys[c])
-                for c in range(calls)]
+    # step variant v: call c takes message set (v * calls + c) % K
+    L = K // math.gcd(K, calls)
+    prepared = [[B.echo_call_prepare(state_of(c), xs[c], *msgs_d[bits_of[c]][(v * calls + c) % K], send_c,
+                                     send_s, own_c, own_s, ys[c])
+                 for c in range(calls)] for v in range(L)]
 
-    def step():
+    def step(v):
         s = torch.cuda.current_stream()
-        for pc in prepared:
+        for pc in prepared[v % L]:
             pc(s)
 
     if args.calibrate:
         calibration_copy(dev)
 
-    for _ in range(max(1, args.warmup)):
-        step()
+    for w in range(max(1, args.warmup)):
+        step(w)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(k)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     graph_ms = None
     if args.graph:
-        g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step()  # warm the side stream before capture
+            step(0)  # warm the side stream before capture
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            step()
-        g.replay()
+        graphs = []
+        for v in range(L):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(v)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
+        for k in range(args.steps):
+            graphs[k % L].replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     best = min(eager_ms, graph_ms) if graph_ms else eager_ms
@@ -726,20 +745,25 @@ def run_workload(args) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {desc}{policy}", "elements": n, "nranks": P, "rank": rank,
-                   "calls_per_step": calls, "calls_8bit": bits_of.count(8)},
+                   "calls_per_step": calls, "calls_8bit": bits_of.count(8), "message_sets": K},
         "us_per_call": round(best * 1e3 / calls, 2),
         "eager_ms_per_step": round(eager_ms, 4),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "pct_hbm_peak": round(100.0 * per_call * calls / (best * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         "algorithmic_bytes_per_call": int(per_call),
     }
+    def host_msgs(c):
+        """host copies of the messages of call c of the first step"""
+        return tuple([None if t is None else t.cpu().numpy() for t in ts]
+                     for ts in msgs_d[bits_of[c]][c % K])
+
     out["cpu_baseline"] = None if args.no_cpu else workload_cpu_baseline(
-        xs, msgs_h, bits_of, P, rank, nstates, args.cpu_seconds)
+        xs, host_msgs, bits_of, P, rank, nstates, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
 
 
-def workload_cpu_baseline(xs, msgs_h, bits_of, P: int, rank: int, nstates: int, budget_s: float):
+def workload_cpu_baseline(xs, msgs_of, bits_of, P: int, rank: int, nstates: int, budget_s: float):
     """The CPU oracle as it stands on the workload's own call sequence, from
     zero state (one state per direction for the training step): the first
     call on one thread, then the step's calls in order on all host cores
@@ -752,12 +776,11 @@ def workload_cpu_baseline(xs, msgs_h, bits_of, P: int, rank: int, nstates: int, 
     n = int(xs[0].numel())
     calls = len(xs)
     T = oracle_threads()
-    sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
-    msgs = {b: (sl(r, 0), sl(r, 1), sl(g, 0), sl(g, 1)) for b, (r, g) in msgs_h.items()}
     x0 = xs[0].cpu().numpy().view(np.uint16)
     mf, ms = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    m0 = msgs_of(0)
     t0 = time.perf_counter()
-    orc.call(P, rank, x0, mf, ms, *msgs[bits_of[0]], threads=1, bits=bits_of[0])
+    orc.call(P, rank, x0, mf, ms, *m0, threads=1, bits=bits_of[0])
     dt1 = time.perf_counter() - t0
     states = [(np.zeros(n, np.float32), np.zeros(n, np.float32)) for _ in range(nstates)]
     done, spent, outs = 0, 0.0, {}
@@ -765,8 +788,9 @@ def workload_cpu_baseline(xs, msgs_h, bits_of, P: int, rank: int, nstates: int, 
         x = xs[done].cpu().numpy().view(np.uint16)
         mf, ms = states[0] if nstates == 1 or done < calls // nstates else states[1]
         b = bits_of[done]
+        m = msgs_of(done)
         t0 = time.perf_counter()
-        outs[b] = orc.call(P, rank, x, mf, ms, *msgs[b], threads=T, out=outs.get(b), bits=b)
+        outs[b] = orc.call(P, rank, x, mf, ms, *m, threads=T, out=outs.get(b), bits=b)
         spent += time.perf_counter() - t0
         done += 1
     return {

@@ -244,6 +244,27 @@ def device_student_t3(n: int, seed: int, device, scale: float = 1e-3):
     return (scale * t).to(torch.bfloat16).view(torch.int16)
 
 
+def device_message(n: int, seed: int, device, scale_lo: float = 0.05, scale_hi: float = 0.55,
+                   bits: int = 4):
+    """A seeded message of n codes drawn on the device, with int4_message's
+    distribution: (codes u8 tensor, scales f32 tensor [n/128]); 4-bit bytes
+    uniform over the 225 without a -8 field, 8-bit bytes over the 255 other
+    than 0x80, scales uniform in [scale_lo, scale_hi)."""
+    import torch
+
+    g = _device_gen(seed, device)
+    if bits == 8:
+        alphabet = np.array([b for b in range(256) if b != 0x80], dtype=np.uint8)
+        nbytes = n
+    else:
+        alphabet = _valid_code_bytes()
+        nbytes = n // 2
+    table = torch.as_tensor(alphabet, device=device)
+    codes = table[torch.randint(0, alphabet.size, (nbytes,), generator=g, device=device)]
+    scales = scale_lo + (scale_hi - scale_lo) * torch.rand(n // 128, generator=g, device=device)
+    return codes.contiguous(), scales.contiguous()
+
+
 def channel_scales(hidden: int, channel_key: int, channel_sigma: float = 1.0,
                    outlier_mult: float = 30.0, outlier_frac: float = 0.001) -> np.ndarray:
     """Per-channel scale exp(N(0, channel_sigma)), a fixed 0.1% subset x mult
