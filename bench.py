@@ -91,15 +91,15 @@ def traffic_from_profile(kernel: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
-def make_messages(N: int, P: int, rank: int, seed: int = 0, which: int = 0):
-    """The seeded incoming stage-1 shards and gathered stage-2 chunks of one
-    call (set `which` of them; set 0 is the workload's own)."""
+def make_messages(N: int, P: int, rank: int, seed: int = 0):
+    """The seeded incoming stage-1 shards and gathered stage-2 chunks of the
+    workload's own call."""
     import numpy as np
 
     from error_compensated_bit_echo_amd import inputs as I
 
     C = N // P
-    tag = ("echo-1gb", seed) if which == 0 else ("echo-1gb", seed, "set", which)
+    tag = ("echo-1gb", seed)
     recv = [None if q == rank else I.int4_message(C, I.stream_key(*tag, "recv", q))
             for q in range(P)]
     # gathered stage-2 chunks carry sums of P contributions: larger scales
@@ -821,7 +821,7 @@ def main() -> int:
                     help="smaller workloads: CPU time budget of the oracle leg")
     ap.add_argument("--no-schedules", action="store_true",
                     help="skip the critical-path comparison (fused / split / uncompensated)")
-    ap.add_argument("--message-sets", type=int, default=1,
+    ap.add_argument("--message-sets", type=int, default=3,
                     help="distinct sets of incoming and gathered messages, cycled call by call")
     ap.add_argument("--cu-split", type=float, default=None,
                     help="also time the split schedule with the compute units partitioned: the "
@@ -859,6 +859,7 @@ def main() -> int:
     import torch
 
     from error_compensated_bit_echo_amd import binding as B
+    from error_compensated_bit_echo_amd import inputs as I
 
     N, P, rank = 1 << args.log2n, args.nranks, 0
     C = N // P
@@ -873,14 +874,21 @@ def main() -> int:
 
     xd = d(x)
     # message sets cycled call by call (set 0 is the workload's own)
-    msets = [(recv, gath)] + [make_messages(N, P, rank, which=k) for k in range(1, args.message_sets)]
+    # set 0 is the workload's own (the oracle leg's); the others are drawn on
+    # the device with the same distributions
     dsets = []
-    for r_h, g_h in msets:
-        rd = [None if m is None else (d(m[0]), d(m[1])) for m in r_h]
-        gd = [None if m is None else (d(m[0]), d(m[1])) for m in g_h]
+    for k in range(args.message_sets):
+        if k == 0:
+            rd = [None if m is None else (d(m[0]), d(m[1])) for m in recv]
+            gd = [None if m is None else (d(m[0]), d(m[1])) for m in gath]
+        else:
+            rd = [None if q == rank else I.device_message(C, I.stream_key("echo-1gb", "set", k, "recv", q), dev)
+                  for q in range(P)]
+            gd = [None if j == rank else I.device_message(C, I.stream_key("echo-1gb", "set", k, "gath", j), dev,
+                                                          scale_lo=0.05 * np.sqrt(P), scale_hi=0.55 * np.sqrt(P))
+                  for j in range(P)]
         dsets.append(([None if m is None else m[0] for m in rd], [None if m is None else m[1] for m in rd],
                       [None if m is None else m[0] for m in gd], [None if m is None else m[1] for m in gd]))
-    del msets
     mf = torch.empty(N, dtype=torch.float32, device=dev)
     ms = torch.empty(N, dtype=torch.float32, device=dev)
     send_c = torch.empty(N // 2, dtype=torch.uint8, device=dev)
