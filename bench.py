@@ -529,7 +529,8 @@ def practical_ceiling(B, torch, stream, nbytes: int = 1 << 30, reps: int = 10) -
 def run_sweep(args) -> int:
     """Time per fused call (rank 0 of P = 8) over message sizes from 2^16 to
     2^29 elements; small sizes replay a captured graph of 64 calls so the
-    figure is the GPU's, not the host's."""
+    figure is the GPU's, not the host's.  Calls cycle a pool of message
+    sets."""
     import torch
 
     from error_compensated_bit_echo_amd import binding as B
@@ -551,9 +552,17 @@ def run_sweep(args) -> int:
             c = torch.where((c >> 4) == 8, c ^ 16, c)
             return c, torch.rand(C // 128, device=dev, generator=gen) * 0.5 + 0.05
 
-        recv = [None if q == rank else msg() for q in range(P)]
-        gath = [None if j == rank else msg() for j in range(P)]
+        # a pool of message sets, cycled call by call: 2^29 bytes or more
+        # (twice the Infinity Cache) where 16 sets reach it, so the larger
+        # sizes read every call's messages from HBM
+        set_bytes = 2 * (P - 1) * (C // 2 + C // 32)
+        nsets = max(2, min(16, -(-(1 << 29) // set_bytes)))
         sl = lambda arr, k: [None if m is None else m[k] for m in arr]  # noqa: E731
+        pool = []
+        for _ in range(nsets):
+            recv = [None if q == rank else msg() for q in range(P)]
+            gath = [None if j == rank else msg() for j in range(P)]
+            pool.append((sl(recv, 0), sl(recv, 1), sl(gath, 0), sl(gath, 1)))
         mf, ms = torch.empty(n, device=dev), torch.empty(n, device=dev)
         st = B.echo_state_init(mf, ms, n, P, rank)
         send_c = torch.empty(n // 2, dtype=torch.uint8, device=dev)
@@ -561,26 +570,25 @@ def run_sweep(args) -> int:
         own_c = torch.empty(C // 2, dtype=torch.uint8, device=dev)
         own_s = torch.empty(C // 128, device=dev)
         y = torch.empty(n, dtype=torch.int16, device=dev)
-        call = B.echo_call_prepare(st, x, sl(recv, 0), sl(recv, 1), sl(gath, 0), sl(gath, 1), send_c,
-                                   send_s, own_c, own_s, y)
-        reps = 64 if log2n < 24 else 8
+        calls = [B.echo_call_prepare(st, x, *m, send_c, send_s, own_c, own_s, y) for m in pool]
+        reps = 64 if log2n < 24 else 8 * nsets
         if log2n < 24:
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
-                for _ in range(reps):
-                    call(side)
+                for i in range(reps):
+                    calls[i % nsets](side)
             torch.cuda.current_stream().wait_stream(side)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for _ in range(reps):
-                    call()
+                for i in range(reps):
+                    calls[i % nsets]()
             run = g.replay
         else:
             def run():
-                for _ in range(reps):
-                    call()
+                for i in range(reps):
+                    calls[i % nsets]()
         run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -593,7 +601,7 @@ def run_sweep(args) -> int:
         rows.append({"elements": n, "us_per_call": round(us, 2),
                      "payload_GBps": round(2.0 * n / (us * 1e-6) / 1e9, 1),
                      "pct_hbm_peak": round(100.0 * step_bytes(n, P) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)})
-        del x, recv, gath, mf, ms, send_c, send_s, own_c, own_s, y, call, st
+        del x, recv, gath, pool, mf, ms, send_c, send_s, own_c, own_s, y, calls, st
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "fused Echo call time vs message size (rank 0 of 8)", "unit": "us",
                       "dtype": "f32", "data": "synthetic", "n_gpus": 1, "sweep": rows}), flush=True)
