@@ -34,6 +34,23 @@ MUTANTS = [
      "float t = rintf(v[i] / s);", "float t = roundf(v[i] / s);"),
     ("scale by a reciprocal multiply", C1,
      "float s = amax / (float)qmax;", "float s = amax * (1.0f / (float)qmax);"),
+    ("group absmax taken over signed values", C1,
+     "float a = fabsf(v[i]);", "float a = v[i];"),
+    ("zero-group rule dropped", C1,
+     "if (s == 0.0f) {", "if (s != s) {"),
+    ("odd groups dequantized with the even neighbour's scale", C1,
+     "return (float)code_at(codes, i, bits) * scales[i / ORC_GROUP];",
+     "return (float)code_at(codes, i, bits) * scales[(i / ORC_GROUP) & ~(int64_t)1];"),
+    ("rank-order sum started from the last rank", C1,
+     """      float acc = dequant(shard_codes[0], shard_scales[0], e, bits);
+      for (int r = 1; r < nranks; ++r) acc = acc + dequant(shard_codes[r], shard_scales[r], e, bits);""",
+     """      float acc = dequant(shard_codes[nranks - 1], shard_scales[nranks - 1], e, bits);
+      for (int r = nranks - 2; r >= 0; --r) acc = acc + dequant(shard_codes[r], shard_scales[r], e, bits);"""),
+    ("reduce-scatter sum started from the last rank", C1,
+     """    float acc = dequant(shard_codes[0], shard_scales[0], i, bits);
+    for (int r = 1; r < nranks; ++r) acc = acc + dequant(shard_codes[r], shard_scales[r], i, bits);""",
+     """    float acc = dequant(shard_codes[nranks - 1], shard_scales[nranks - 1], i, bits);
+    for (int r = nranks - 2; r >= 0; --r) acc = acc + dequant(shard_codes[r], shard_scales[r], i, bits);"""),
     ("nibbles swapped in a byte", C1,
      "codes[k] = (uint8_t)(lo | (hi << 4));", "codes[k] = (uint8_t)(hi | (lo << 4));"),
     ("wrong sign extension of a nibble", C1,

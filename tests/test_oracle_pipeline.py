@@ -760,3 +760,23 @@ def test_zero_padded_tail_stays_zero_and_padding_is_transparent(bits):
         runs[n] = dict(x0=xs0, **first)
     assert np.array_equal(runs[1536]["y"], runs[3072]["y"])
     np.testing.assert_allclose(runs[1536]["mf_sum"], runs[3072]["mf_sum"], rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("dq, s_want", [((2.0 ** 24, 1.0, 1.0), 2.0 ** 24),
+                                         ((1.0, 1.0, 2.0 ** 24), 2.0 ** 24 + 2.0)])
+def test_reduce_sums_in_rank_order_from_rank_0(dq, s_want):
+    """The chunk sum is the binary32 left fold d_0 + d_1 + ... + d_{P-1}
+    (reading 8).  With d = (2^24, 1, 1) the fold absorbs both ones (2^24 + 1
+    ties to the even 2^24); with d = (1, 1, 2^24) it keeps them (2 + 2^24 is a
+    binary32 value).  The same values summed in any other order fail one of
+    the two cases.  S is read back exactly as f32(y) - e, since y lies within
+    a factor of two of S."""
+    P, n = 3, 128
+    codes = [np.zeros(n, np.uint8) for _ in range(P)]  # 8-bit codes, one byte each
+    for c in codes:
+        c[0] = 1  # element 0: code 1 in every shard, so d_q is shard q's scale
+    scales = [np.array([v], np.float32) for v in dq]
+    _, _, y, e2 = orc.reduce_chunk(codes, scales, n, bits=8)
+    assert float(orc.bf16_to_f32(y[:1])[0]) - float(e2[0]) == s_want
+    y_rs, e_rs = orc.reduce_chunk_sum(codes, scales, n, bits=8)
+    assert float(orc.bf16_to_f32(y_rs[:1])[0]) - float(e_rs[0]) == s_want
