@@ -61,6 +61,15 @@ MUTANTS = [
      "return bits == 8 ? ORC_QMAX8 : ORC_QMAX;", "return bits == 8 ? ORC_QMAX8 - 1 : ORC_QMAX;"),
     ("correction subtracts the slow average", C1,
      "return (ORC_W_FAST * mf) + (ORC_W_SLOW * ms);", "return (ORC_W_FAST * mf) - (ORC_W_SLOW * ms);"),
+    ("correction halves the summed averages", C1,
+     "return (ORC_W_FAST * mf) + (ORC_W_SLOW * ms);", "return ORC_W_FAST * (mf + ms);"),
+    ("slow average refreshed in increment form", C1,
+     "m_slow[i] = (ORC_BETA_SLOW * m_slow[i]) + (ORC_ALPHA_SLOW * r);",
+     "m_slow[i] = m_slow[i] + (ORC_ALPHA_SLOW * (r - m_slow[i]));"),
+    ("exit pass truncates to bf16", C1,
+     "for (int64_t i = 0; i < n; ++i) y[i] = orc_f32_to_bf16(dequant(codes, scales, i, bits));",
+     "for (int64_t i = 0; i < n; ++i) { float f = dequant(codes, scales, i, bits); uint32_t u; "
+     "memcpy(&u, &f, sizeof u); y[i] = (uint16_t)(u >> 16); }"),
     ("correction added to the input", C1,
      "return xf - corr;", "return xf + corr;"),
     ("stage-1 residual with the wrong sign", C1,

@@ -214,3 +214,51 @@ def test_update_from_zero_state_is_alpha_times_residual():
     r[n // P:2 * n // P] = r[n // P:2 * n // P] + e2
     assert np.array_equal(mf, (0.5 * r.astype(np.float64)).astype(np.float32))
     assert np.array_equal(ms, (0.125 * r.astype(np.float64)).astype(np.float32))
+
+
+def _round_f32(q: Fraction) -> float:
+    """The binary32 value nearest to the exact rational q (ties to the even
+    significand), found by exact comparison among q's neighbourhood; q is
+    nonzero and inside the normal range here."""
+    f = np.float32(float(q))
+    cands = [f]
+    for _ in range(2):
+        cands = [np.nextafter(cands[0], np.float32(-np.inf))] + cands + \
+                [np.nextafter(cands[-1], np.float32(np.inf))]
+    best = None
+    for c in cands:
+        d = abs(Fraction(float(c)) - q)
+        even = (int(np.float32(c).view(np.uint32)) & 1) == 0
+        if best is None or d < best[0] or (d == best[0] and even):
+            best = (d, c)
+    return float(best[1])
+
+
+def test_update_rounds_each_operation_in_the_written_order():
+    """The refresh is m <- (B * m) + (A * r) with each product and the sum
+    rounded once, in that order (reading 19), checked against exact rational
+    arithmetic with IEEE rounding applied step by step.  B_S = 7/8 makes
+    B_S * m inexact, so a reassociated form such as m + A (r - m) rounds
+    differently on many elements."""
+    rng = np.random.default_rng(19)
+    n, P, rank = 128 * 16, 4, 2
+    x = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).to(torch.bfloat16)
+    xb = x.view(torch.int16).numpy().view(np.uint16).copy()
+    mf = (rng.standard_normal(n) * 0.3).astype(np.float32)
+    ms = (rng.standard_normal(n) * 0.3).astype(np.float32)
+    codes, scales = orc.encode(xb, mf, ms)
+    e2 = (rng.standard_normal(n // P) * 1e-2).astype(np.float32)
+    mf0, ms0 = mf.copy(), ms.copy()
+    r = orc.update(xb, mf, ms, codes, scales, e2, nranks=P, rank=rank, want_r=True)
+    BF, AF = Fraction(float(orc.BETA_FAST)), Fraction(float(orc.ALPHA_FAST))
+    BS, AS = Fraction(float(orc.BETA_SLOW)), Fraction(float(orc.ALPHA_SLOW))
+
+    def refresh(B, A, m, ri):
+        bm = _round_f32(B * Fraction(float(m))) if m != 0 else 0.0
+        ar = _round_f32(A * Fraction(float(ri))) if ri != 0 else 0.0
+        s = Fraction(bm) + Fraction(ar)
+        return _round_f32(s) if s != 0 else 0.0
+
+    for i in range(n):
+        assert float(mf[i]) == refresh(BF, AF, mf0[i], r[i]), i
+        assert float(ms[i]) == refresh(BS, AS, ms0[i], r[i]), i
