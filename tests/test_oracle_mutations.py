@@ -32,6 +32,10 @@ MUTANTS = [
      "if (dropped > 0x8000u) {", "if (dropped >= 0x8000u) {"),
     ("codes round half away from zero", C1,
      "float t = rintf(v[i] / s);", "float t = roundf(v[i] / s);"),
+    ("codes by a reciprocal multiply", C1,
+     "float t = rintf(v[i] / s);", "float t = rintf(v[i] * (1.0f / s));"),
+    ("input corrected one average at a time", C1,
+     "return xf - corr;", "return (xf - (ORC_W_FAST * mf)) - (ORC_W_SLOW * ms);"),
     ("scale by a reciprocal multiply", C1,
      "float s = amax / (float)qmax;", "float s = amax * (1.0f / (float)qmax);"),
     ("group absmax taken over signed values", C1,
