@@ -100,6 +100,33 @@ def test_reduce_shard(P, k, any_byte, bits):
     eq(g.host(c2, np.uint8), wc, "codes2 without y/e2")
 
 
+@pytest.mark.parametrize("dq, s_want", [((2.0 ** 24, 1.0, 1.0), 2.0 ** 24),
+                                         ((1.0, 1.0, 2.0 ** 24), 2.0 ** 24 + 2.0)])
+def test_reduce_sums_in_rank_order_from_rank_0(dq, s_want):
+    """The GPU's chunk sums are the binary32 left fold from rank 0: with
+    dequantized values (2^24, 1, 1) the ones are absorbed, with (1, 1, 2^24)
+    they are kept.  S is read back exactly as f32(y) - e (y is within a
+    factor of two of S), for both the requantizing and the bf16 sum."""
+    g = gu()
+    P, n = 3, 128
+    codes = [np.zeros(n, np.uint8) for _ in range(P)]
+    for c in codes:
+        c[0] = 1
+    scales = [np.array([v], np.float32) for v in dq]
+    oc, os_, y, e = g.empty_u8(n), g.empty_f32(1), g.empty_bf16(n), g.empty_f32(n)
+    B.echo_reduce_shard([g.dev(c) for c in codes], [g.dev(s) for s in scales], oc, os_, y, e,
+                        chunk_n=n, bits=8)
+    yh, eh = g.host(y, np.uint16), g.host(e, np.float32)
+    assert float(orc.bf16_to_f32(yh[:1])[0]) - float(eh[0]) == s_want
+    wc, ws, wy, we = orc.reduce_chunk(codes, scales, n, bits=8)
+    eq(yh, wy, "y")
+    eq(eh, we, "e2")
+    y2, e2 = g.empty_bf16(n), g.empty_f32(n)
+    B.echo_reduce_shard_sum([g.dev(c) for c in codes], [g.dev(s) for s in scales], y2, e2, chunk_n=n,
+                            bits=8)
+    assert float(orc.bf16_to_f32(g.host(y2, np.uint16)[:1])[0]) - float(g.host(e2, np.float32)[0]) == s_want
+
+
 @pytest.mark.parametrize("k", [1, 3, 4, 5, 1023, 4099])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_decode(k, bits):
