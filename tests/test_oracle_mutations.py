@@ -55,6 +55,14 @@ MUTANTS = [
     for (int r = 1; r < nranks; ++r) acc = acc + dequant(shard_codes[r], shard_scales[r], i, bits);""",
      """    float acc = dequant(shard_codes[nranks - 1], shard_scales[nranks - 1], i, bits);
     for (int r = nranks - 2; r >= 0; --r) acc = acc + dequant(shard_codes[r], shard_scales[r], i, bits);"""),
+    ("stage-2 requantized to 4-bit levels at 8 bits", C1,
+     "orc_quantize_group_q(S, ORC_GROUP, qmax_of(bits), q, &scales2[g], 2);",
+     "orc_quantize_group_q(S, ORC_GROUP, ORC_QMAX, q, &scales2[g], 2);"),
+    ("every rank sent the own chunk's message", C1,
+     "memcpy(send_codes + j * cb, codes1 + j * cb, (size_t)cb);",
+     "memcpy(send_codes + j * cb, codes1 + rank * cb, (size_t)cb);"),
+    ("bf16 widened with a stray low bit", C1,
+     "uint32_t u = (uint32_t)h << 16;", "uint32_t u = ((uint32_t)h << 16) | 0x8000u;"),
     ("nibbles swapped in a byte", C1,
      "codes[k] = (uint8_t)(lo | (hi << 4));", "codes[k] = (uint8_t)(hi | (lo << 4));"),
     ("wrong sign extension of a nibble", C1,
