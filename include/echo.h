@@ -160,7 +160,7 @@ int echo_encode(const echo_state* st, const uint16_t* x, uint8_t* codes, float* 
  * requantize S like the entry pass -> out_codes[chunk_n/2], out_scales
  * [chunk_n/128].  Optional outputs (NULL to skip): out_y[chunk_n] =
  * bf16(code2*s2) rounded to nearest even, out_e2[chunk_n] = f32(y) - S.
- * chunk_n > 0 and chunk_n % 128 == 0. */
+ * chunk_n % 128 == 0; chunk_n == 0 is a no-op. */
 int echo_reduce_shard(int32_t nranks, int64_t chunk_n, int32_t bits,
                       const uint8_t* const* shard_codes, const float* const* shard_scales,
                       uint8_t* out_codes, float* out_scales, uint16_t* out_y, float* out_e2,
@@ -211,9 +211,9 @@ int echo_call_entry(const echo_state* st, const uint16_t* x, uint8_t* send_codes
 /* The entry phase restricted to chunks [chunk_begin, chunk_end), the own
  * chunk still skipped ("Tensor-parallel traffic drops to 4 bits",
  * Interpretation, as echo_call_entry; the split by chunk is this library's,
- * so that sending can overlap encoding): for each such chunk j exactly what echo_call_entry
- * does to chunk j (its part of send_codes / send_scales and of the
- * averages), nothing else.  Ranges that cover [0, P) once, in any order and
+ * so that sending can overlap encoding): for each such chunk j exactly what
+ * echo_call_entry does to chunk j (its part of send_codes / send_scales and
+ * of the averages), nothing else.  Ranges that cover [0, P) once, in any order and
  * on any streams the caller orders before the reduce phase, together equal
  * one echo_call_entry; a transport can send chunk j to rank j while later
  * chunks are still being encoded.  Buffers are the full-size ones of
@@ -227,8 +227,9 @@ int echo_call_entry_range(const echo_state* st, const uint16_t* x, int32_t chunk
  * Parallel Communication", Abstract: the codes are summed in a wide format
  * and requantized, a value's second and last quantization; "Tensor-parallel
  * traffic drops to 4 bits", Interpretation: forming the sum exposes the error
- * the call injected, which refreshes the averages): correction and stage-1 quantization of
- * the own elements (kept in registers, never stored), the rank-order sum with
+ * the call injected, which refreshes the averages): correction and stage-1
+ * quantization of the own elements (kept in registers, never stored), the
+ * rank-order sum with
  * the P-1 incoming shards recv_codes[q] / recv_scales[q] (host arrays of
  * nranks device pointers; slot `rank` is ignored and may be NULL; each shard
  * covers chunk `rank`: codes[n/P/2], scales[n/P/128]), requantization into
