@@ -62,6 +62,7 @@ def source_hash() -> str:
 
     h = hashlib.sha256()
     for rel in ("error_compensated_bit_echo_amd/csrc/echo_device.h",
+                "error_compensated_bit_echo_amd/csrc/launch_shape.h",
                 "error_compensated_bit_echo_amd/csrc/echo_api.hip",
                 "error_compensated_bit_echo_amd/build.py"):
         with open(os.path.join(ROOT, rel)) as f:
