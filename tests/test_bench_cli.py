@@ -65,3 +65,14 @@ def test_serving_policy_only_for_serving_workloads():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--message-sets", "0"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "--message-sets" in r.stderr
+
+
+def test_committed_traffic_profile_matches_the_kernel_sources():
+    """The counted HBM traffic in profiles/ was taken on the kernels as they
+    stand: the bench reports roofline.traffic only while the kernel and launch
+    sources hash to the value recorded with the counters."""
+    import bench
+
+    for kernel in ("entry", "reduce", "exit"):
+        t = bench.traffic_from_profile(kernel, "1gb")
+        assert t is not None, f"profiles/traffic.json is stale for {kernel}: retake the HBM counters"
